@@ -1,0 +1,126 @@
+"""Oracle for the fused linear cross-entropy forward -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package. It is a plain float64 CPU
+implementation of the definition on the page "A fused forward kernel for
+linear cross-entropy on Apple GPUs" (section 1): Z = H W^T and
+loss_i = logsumexp(Z_i) - Z_{i, y_i}. The arithmetic lives in
+``flce_oracle.c`` (plain C, OpenMP over rows); this module only builds it and
+marshals arguments. It shares no code with the GPU library.
+
+Pins (what ties it to something other than itself) are the ``not gpu`` tests
+in ``tests/test_oracle_pins.py`` and ``tests/test_oracle_mutants.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "flce_oracle.c")
+_LIB = os.path.join(_HERE, "_build", "liboracle.so")
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"])
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str | None = None):
+    """Load the oracle library, building it first if nothing is built."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _LIB
+    if not os.path.exists(p):
+        build(out=p)
+    lib = ctypes.CDLL(p)
+    lib.oracle_lce_forward.restype = ctypes.c_int
+    lib.oracle_lce_forward.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_num_threads.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _as_numpy(x):
+    """Host array with the exact bits of x: bf16 -> uint16, fp32 -> float32."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach()
+            if x.device.type != "cpu":
+                x = x.cpu()
+            x = x.contiguous()
+            if x.dtype == torch.bfloat16:
+                return x.view(torch.int16).numpy().view(np.uint16), 0
+            if x.dtype == torch.float32:
+                return x.numpy(), 1
+            if x.dtype == torch.int32:
+                return x.numpy(), None
+            raise TypeError(f"unsupported dtype {x.dtype}")
+    except ImportError:
+        pass
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return x, 0
+    if x.dtype == np.float32:
+        return x, 1
+    if x.dtype == np.int32:
+        return x, None
+    raise TypeError(f"unsupported dtype {x.dtype}")
+
+
+def num_threads() -> int:
+    return int(load().oracle_num_threads())
+
+
+def forward(H, W, y, rows=None, lib=None):
+    """Return (loss, lse, z_target) as float64 numpy arrays.
+
+    H: (N, D), W: (V, D), both bfloat16 or both float32 (torch CPU/GPU
+    tensors, or numpy uint16 bit patterns / float32); y: int32 (N).
+    rows: optional sequence of row indices; outputs follow that order.
+    """
+    lib = lib or load()
+    h, dt_h = _as_numpy(H)
+    w, dt_w = _as_numpy(W)
+    t, _ = _as_numpy(y)
+    if dt_h != dt_w or dt_h is None:
+        raise TypeError("H and W must share a floating dtype")
+    if t.dtype != np.int32:
+        raise TypeError("targets must be int32")
+    N, D = h.shape
+    V, D2 = w.shape
+    if D2 != D or t.shape != (N,):
+        raise ValueError("shape mismatch")
+    if rows is None:
+        R = N
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = rows_arr.shape[0]
+    loss = np.empty(R, np.float64)
+    lse = np.empty(R, np.float64)
+    zt = np.empty(R, np.float64)
+    rc = lib.oracle_lce_forward(
+        h.ctypes.data, w.ctypes.data, t.ctypes.data, N, D, V, dt_h,
+        rows_arr.ctypes.data if rows_arr is not None else None, R,
+        loss.ctypes.data, lse.ctypes.data, zt.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return loss, lse, zt

@@ -1,0 +1,116 @@
+/*
+ * Oracle for the linear cross-entropy forward. TEST INFRASTRUCTURE ONLY:
+ * the tests, the smoke check and the benchmark's CPU-baseline leg use it to
+ * judge the GPU library; the library never calls it.
+ *
+ * It is the plain definition from "A fused forward kernel for linear
+ * cross-entropy on Apple GPUs" (section 1, the definition of plain
+ * cross-entropy): with H an (N, D) matrix of hidden states and W a (V, D)
+ * output projection, the logits are Z = H W^T and, for the target y_i,
+ *     loss_i = logsumexp(Z_i) - Z_{i, y_i}.
+ * The same section states that only two per-row statistics are needed, the
+ * log-sum-exp and the target logit; both are returned.
+ *
+ * Each selected row is computed independently, in float64, with nothing
+ * streamed or tiled: the V logits of the row are materialised in a buffer,
+ * then the maximum M, then S = sum_v exp(z_v - M) in vocabulary order, then
+ * lse = M + ln S and loss = lse - z_y. (The shift by M is the textbook
+ * two-pass form of logsumexp; it changes nothing in exact arithmetic.)
+ *
+ * Readings where the page is silent:
+ *   - the logarithm is natural (the page writes exp and logsumexp);
+ *   - a target outside [0, V) has no defined loss: loss = NaN, lse is still
+ *     returned and z_target = NaN;
+ *   - there is no bias, scale, softcap, smoothing or reduction over rows.
+ *
+ * Inputs are the exact bit patterns the GPU reads: bfloat16 (dtype 0) or
+ * IEEE fp32 (dtype 1), row-major, D contiguous. Each element is widened
+ * exactly to double; products of two such values are exact in double, so the
+ * only rounding is the float64 summation.
+ *
+ * Rows run in parallel with OpenMP; every row is still the same sequential
+ * computation whatever the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double widen(const void* base, int dtype, int64_t idx) {
+  if (dtype == 0) {
+    uint32_t u = (uint32_t)((const uint16_t*)base)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)base)[idx];
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/*
+ * rows: R row indices into [0, N) (NULL means rows 0..N-1 with R = N).
+ * Writes loss[r], lse[r], z_target[r] for r in [0, R).
+ * Returns 0, or -1 on an invalid argument or a failed allocation.
+ */
+int oracle_lce_forward(const void* H, const void* W, const int32_t* y,
+                       int64_t N, int64_t D, int64_t V, int dtype,
+                       const int64_t* rows, int64_t R,
+                       double* loss, double* lse, double* z_target) {
+  if (N < 0 || D < 1 || V < 1 || R < 0 || (dtype != 0 && dtype != 1)) return -1;
+  if (!rows) R = N;
+  if (R > 0 && (!H || !W || !y || !loss || !lse || !z_target)) return -1;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* z = (double*)malloc((size_t)V * sizeof(double));
+    if (!z) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+      if (!z) continue;
+      int64_t i = rows ? rows[r] : r;
+      if (i < 0 || i >= N) {
+#pragma omp atomic write
+        failed = 1;
+        continue;
+      }
+      /* Z_i = H_i W^T, one logit per vocabulary row. */
+      for (int64_t v = 0; v < V; ++v) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+          acc += widen(H, dtype, i * D + d) * widen(W, dtype, v * D + d);
+        z[v] = acc;
+      }
+      /* logsumexp(Z_i), two passes: the maximum, then the shifted sum. */
+      double M = z[0];
+      for (int64_t v = 1; v < V; ++v)
+        if (z[v] > M || isnan(z[v])) M = z[v];
+      double S = 0.0;
+      for (int64_t v = 0; v < V; ++v) S += exp(z[v] - M);
+      double l = M + log(S);
+      lse[r] = l;
+      int64_t t = (int64_t)y[i];
+      if (t >= 0 && t < V) {
+        z_target[r] = z[t];
+        loss[r] = l - z[t];
+      } else {
+        z_target[r] = NAN;
+        loss[r] = NAN;
+      }
+    }
+    free(z);
+  }
+  return failed ? -1 : 0;
+}

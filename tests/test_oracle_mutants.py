@@ -1,0 +1,59 @@
+"""Plant plausible mistakes in copies of the oracle and check the pins catch each.
+
+Every mutant is a textual edit of oracle/flce_oracle.c compiled to a private
+library on the CPU; the real oracle is never modified. A mutant that passes
+every pin would mean the pins cannot tell that mistake from the definition.
+"""
+import os
+import tempfile
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "flce_oracle.c")
+
+MUTANTS = {
+    "drop_last_word": ("for (int64_t v = 0; v < V; ++v) S += exp(z[v] - M);",
+                       "for (int64_t v = 0; v < V - 1; ++v) S += exp(z[v] - M);"),
+    "drop_first_word": ("for (int64_t v = 0; v < V; ++v) S += exp(z[v] - M);",
+                        "for (int64_t v = 1; v < V; ++v) S += exp(z[v] - M);"),
+    "lse_sign": ("double l = M + log(S);", "double l = M - log(S);"),
+    "log_base2": ("double l = M + log(S);", "double l = M + log2(S);"),
+    "loss_sign": ("loss[r] = l - z[t];", "loss[r] = z[t] - l;"),
+    "no_max_shift": ("S += exp(z[v] - M);\n      double l = M + log(S);",
+                     "S += exp(z[v]);\n      double l = log(S);"),
+    "zero_init_max": ("double M = z[0];", "double M = 0.0;"),
+    "transposed_W": ("widen(W, dtype, v * D + d)", "widen(W, dtype, d * V + v)"),
+    "transposed_H": ("widen(H, dtype, i * D + d)", "widen(H, dtype, d * N + i)"),
+    "drop_first_feature": ("for (int64_t d = 0; d < D; ++d)", "for (int64_t d = 1; d < D; ++d)"),
+    "neighbour_target": ("loss[r] = l - z[t];", "loss[r] = l - z[(t + 1) % V];"),
+    "lse_minus_target_twice": ("lse[r] = l;", "lse[r] = l - z[0];"),
+    "bf16_high_half_wrong": ("(uint32_t)((const uint16_t*)base)[idx] << 16",
+                             "(uint32_t)((const uint16_t*)base)[idx] << 15"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    old, new = MUTANTS[name]
+    with open(SRC) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site for {name} not found exactly once"
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "mutant.c")
+        with open(src, "w") as f:
+            f.write(text.replace(old, new))
+        lib = oracle.load(oracle.build(src=src, out=os.path.join(d, "libmutant.so")))
+
+        def fwd(H, W, y, rows=None):
+            return oracle.forward(H, W, y, rows=rows, lib=lib)
+
+        caught = []
+        for pin in ALL_PINS:
+            try:
+                pin(fwd)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin.__name__)
+        assert caught, f"no pin catches mutant {name}"
