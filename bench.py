@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused linear cross-entropy forward on one MI355X.
+
+One step = one full forward (the partials launch, then the merge launch) over
+the workload's synthetic inputs, already resident in device memory. Prints one
+JSON line:
+
+  value        tokens/s over the K timed steps (N tokens per step)
+  roofline     the partials kernel (the dominant launch) against the bf16
+               dense matrix-core peak: achieved = 2*N*V*D FLOP / its average
+               duration, measured with HIP events on the stream it runs on
+  cpu_baseline the float64 CPU oracle on a bounded row sample of the same
+               workload, on the host's cores (a reported baseline only)
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prod_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# Published MI355X dense peaks (TFLOP/s): bf16 matrix 2516.6 (256 CU x 2.4 GHz x
+# 4096 FLOP/clk/CU), fp32 matrix 157.3.
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}
+HBM_PEAK_GBS = 8000.0
+METRIC = "tokens/s + % bf16 MFMA peak, fused LCE fwd N=8192 D=4096 V=151936"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_flce_partials_prod_bf16.json")
+KERNEL_SRC = os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "flce.hip")
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per partials launch from the committed rocprofv3 counter runs,
+    or None when they were taken on a different kernel source or workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha() or t.get("workload") != workload:
+        return None
+    return {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
+            "total_bytes": t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"],
+            "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+
+
+def cpu_baseline(H, W, y, w, target_seconds: float, max_rows: int):
+    """Time the oracle on a row sample sized for about target_seconds of wall time."""
+    import oracle
+    import workloads
+    Hc, Wc, yc = H.cpu(), W.cpu(), y.cpu()
+    threads = oracle.num_threads()
+    # calibrate on one row per thread, then size the sample
+    probe = workloads.subset_rows(w.N, max(1, threads), seed=777).numpy()[:threads]
+    t0 = time.perf_counter()
+    oracle.forward(Hc, Wc, yc, rows=probe)
+    t_probe = time.perf_counter() - t0
+    per_row_wall = t_probe / len(probe)
+    rows_n = int(max(len(probe), min(max_rows, target_seconds / max(per_row_wall, 1e-9))))
+    rows_n = max(threads, (rows_n // threads) * threads)
+    rows = workloads.subset_rows(w.N, rows_n, seed=778).numpy()
+    t0 = time.perf_counter()
+    oracle.forward(Hc, Wc, yc, rows=rows)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.N} rows (first/last {max(1, len(rows) // 8)} plus seeded "
+                      f"random), each a full float64 row of {w.V} logits over D={w.D}; "
+                      f"{dt:.2f} s wall",
+            "seconds": dt, "rows": len(rows)}
+
+
+def copy_calibration(nbytes: int, reps: int):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prod_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle's row sample")
+    ap.add_argument("--cpu-max-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of BYTES bytes (counter scaling), then exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward shards by rows with no "
+              "communication, and multi-GPU runs are not part of this build. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
+
+    import linear_cross_entropy_amd as flce
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
+    H, W, y = workloads.make(w, dev)
+    loss = torch.empty(w.N, device=dev)
+    lse = torch.empty(w.N, device=dev)
+    ws = flce.workspace(w.N, w.D, w.V, w.dtype, dev)
+    plan = flce.flce_get_plan(w.N, w.D, w.V, w.dtype)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+
+    def step():
+        flce.flce_partials(H, W, y, ws, stream=stream)
+        flce.flce_merge(y, w.D, w.V, w.dtype, ws, loss=loss, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        flce.flce_partials(H, W, y, ws, stream=stream)
+        b.record(stream)
+        flce.flce_merge(y, w.D, w.V, w.dtype, ws, loss=loss, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [a.elapsed_time(b) for a, b in ev]
+    kernel_ms_sorted = sorted(kernel_ms)
+    avg_ms = sum(kernel_ms) / len(kernel_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = w.flops
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = traffic_from_profile(w.name)
+    sanity = bool(torch.isfinite(loss).all().item() and torch.isfinite(lse).all().item())
+
+    result = {
+        "metric": METRIC,
+        "value": w.N * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded; H ~ N(0,1), W ~ N(0,0.02) rounded to bf16, uniform int32 targets)",
+        "config": {"workload": w.name, "N": w.N, "D": w.D, "V": w.V, "input_dtype": w.dtype,
+                   "tile_vocab": plan["tile_vocab"], "tile_tokens": plan["tile_tokens"],
+                   "chunks": plan["chunks"], "grid": plan["grid"],
+                   "workspace_bytes": plan["workspace_bytes"]},
+        "mfma_fraction_of_step": flops / (ms_per_step * 1e-3) / 1e12 / peak,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "flce_partials_kernel",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": traffic,
+            "algorithmic_flop_per_launch": flops,
+            "kernel_ms_avg": avg_ms,
+            "kernel_ms_median": kernel_ms_sorted[len(kernel_ms) // 2],
+            "kernel_ms_min": kernel_ms_sorted[0],
+        },
+        "outputs_finite": sanity,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
+        cb = cpu_baseline(H, W, y, w, args.cpu_seconds, args.cpu_max_rows)
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,133 @@
+/*
+ * flce.h -- fused linear cross-entropy forward on AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined on the page "A fused forward kernel for
+ * linear cross-entropy on Apple GPUs" (section 1): for hidden states H
+ * (N x D) and an output projection W (V x D) the logits are Z = H W^T, and
+ * for each token i with target y_i
+ *
+ *     lse_i  = logsumexp_v Z[i, v]          (natural logarithm)
+ *     loss_i = lse_i - Z[i, y_i].
+ *
+ * The same section observes that only these two per-row statistics are
+ * needed, so the library streams vocabulary tiles of Z through the online
+ * (running max m, scaled sum s) update of that section and never stores the
+ * N x V logits: device memory beyond the caller's buffers is a workspace of
+ * (2*C + 1)*N floats, where C (the number of vocabulary chunks per row
+ * block) is at most a few hundred.
+ *
+ * Conventions for every entry point:
+ *   - H, W, targets, loss_out, lse_out and workspace are DEVICE pointers owned
+ *     by the caller. The library never frees them and keeps none of them
+ *     after the call returns.
+ *   - H is N x D and W is V x D, row-major and dense (row stride D elements),
+ *     both of `dtype`. They must be 16-byte aligned and D * sizeof(element)
+ *     must be a multiple of 16 (D % 8 == 0 for bf16, D % 4 == 0 for fp32).
+ *   - targets is int32[N]; loss_out and lse_out are float32[N]; lse_out may be
+ *     NULL when only the loss is wanted.
+ *   - A target outside [0, V) is not an error: that row's loss is NaN and its
+ *     lse is still written. NaN or Inf inputs propagate to the affected rows.
+ *   - stream is a hipStream_t passed as void*; NULL means the default stream.
+ *     Work is enqueued on it and the call returns without waiting; results
+ *     are valid once the stream has completed.
+ *   - Errors are reported only through the returned status (no exceptions,
+ *     no abort); on an error status nothing has been enqueued.
+ *   - All entry points are thread-safe and reentrant. Concurrent calls may
+ *     share H and W but not outputs or a workspace.
+ *   - Accumulation is fp32 (bf16 x bf16 and fp32 x fp32 products on the
+ *     matrix cores); outputs are fp32.
+ */
+#ifndef FLCE_H
+#define FLCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FLCE_BF16 = 0, FLCE_FP32 = 1 } flce_dtype_t;
+
+typedef enum {
+  FLCE_OK = 0,
+  FLCE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, small workspace */
+  FLCE_ERR_UNSUPPORTED = -2, /* unknown dtype, D*elem not a multiple of 16, sizes past int32 */
+  FLCE_ERR_HIP = -3,         /* a HIP runtime call or a kernel launch failed */
+  FLCE_ERR_OOM = -4          /* the stream-ordered workspace allocation failed */
+} flce_status_t;
+
+/* How a shape is split into work. Filled by flce_get_plan (diagnostics). */
+typedef struct {
+  int32_t tile_vocab;      /* vocabulary rows per tile (BV) */
+  int32_t tile_tokens;     /* tokens per tile (BT) */
+  int32_t row_blocks;      /* ceil(N / BT) */
+  int32_t vocab_tiles;     /* ceil(V / BV) */
+  int32_t chunks;          /* C: vocabulary chunks per row block */
+  int32_t grid;            /* workgroups of the partials kernel */
+  int32_t xcd_rows;        /* row blocks per XCD group */
+  int32_t xcd_chunks;      /* chunks per XCD group */
+  int32_t threads;         /* threads per workgroup of the partials kernel */
+  int32_t lds_bytes;       /* LDS per workgroup */
+  size_t workspace_bytes;  /* flce_workspace_bytes for the shape */
+} flce_plan_t;
+
+/*
+ * Loss and lse for every row: the whole forward (partials, then merge).
+ * Gets its workspace with hipMallocAsync on `stream` and releases it with
+ * hipFreeAsync on the same stream (FLCE_ERR_OOM if that allocation fails).
+ * N == 0 is a no-op returning FLCE_OK.
+ */
+int flce_forward(const void* H, const void* W, const int32_t* targets,
+                 int64_t N, int64_t D, int64_t V, int dtype,
+                 float* loss_out, float* lse_out, void* stream);
+
+/* Workspace bytes flce_forward_ws needs for a shape (0 for N == 0, and 0 for
+ * an invalid or unsupported shape). */
+size_t flce_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
+
+/*
+ * As flce_forward, with a caller-provided device workspace of at least
+ * flce_workspace_bytes(N, D, V, dtype) bytes, 256-byte aligned
+ * (FLCE_ERR_INVALID_ARG otherwise). Allocates nothing.
+ */
+int flce_forward_ws(const void* H, const void* W, const int32_t* targets,
+                    int64_t N, int64_t D, int64_t V, int dtype,
+                    float* loss_out, float* lse_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The first of the two launches of flce_forward_ws, on its own: the fused
+ * tile contraction Z_tile = H_blk W_blk^T with the online (m, s) update and
+ * the target-logit capture (page section 1, the update equations). Writes,
+ * into the workspace, one (m, s) pair per (row, chunk) and the target logit
+ * per row. Useful for timing the contraction apart from the merge.
+ */
+int flce_partials(const void* H, const void* W, const int32_t* targets,
+                  int64_t N, int64_t D, int64_t V, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The second launch: combines the C partial (m, s) pairs of each row into
+ * lse = M + ln(sum_c s_c e^(m_c - M)) with M = max_c m_c (the page's update
+ * applied between chunks), and loss = lse - z_y. Reads a workspace filled
+ * by flce_partials for the same (N, D, V, dtype) and targets.
+ */
+int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtype,
+               float* loss_out, float* lse_out,
+               const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tile plan for a shape; FLCE_ERR_INVALID_ARG/UNSUPPORTED as flce_forward. */
+int flce_get_plan(int64_t N, int64_t D, int64_t V, int dtype, flce_plan_t* plan);
+
+/* Static text for a status code; never NULL. */
+const char* flce_status_string(int status);
+
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int flce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H */

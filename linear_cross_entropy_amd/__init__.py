@@ -1,0 +1,221 @@
+"""Python binding of libflce.so, the fused linear cross-entropy forward for
+AMD Instinct MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/flce.h``. PyTorch supplies the
+device memory and the stream. The functions keep the C names:
+
+    flce_forward(H, W, targets, loss=None, lse=None, stream=None) -> (loss, lse)
+    flce_forward_ws(H, W, targets, workspace, loss=None, lse=None, stream=None)
+    flce_partials(H, W, targets, workspace, stream=None)
+    flce_merge(targets, D, V, dtype, workspace, loss=None, lse=None, stream=None)
+    flce_workspace_bytes(N, D, V, dtype) -> int
+    flce_get_plan(N, D, V, dtype) -> dict
+    flce_status_string(status) -> str
+    flce_version() -> int
+
+The operation (page "A fused forward kernel for linear cross-entropy on
+Apple GPUs", section 1): with logits Z = H W^T, lse_i = logsumexp(Z_i) and
+loss_i = lse_i - Z[i, y_i], both fp32 per token.
+
+If the library has not been built, importing this package raises: there is
+no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libflce.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python linear_cross_entropy_amd/_build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+FLCE_BF16 = 0
+FLCE_FP32 = 1
+FLCE_OK = 0
+FLCE_ERR_INVALID_ARG = -1
+FLCE_ERR_UNSUPPORTED = -2
+FLCE_ERR_HIP = -3
+FLCE_ERR_OOM = -4
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+
+_lib.flce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]
+_lib.flce_forward.restype = _i32
+_lib.flce_forward_ws.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.flce_forward_ws.restype = _i32
+_lib.flce_partials.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]
+_lib.flce_partials.restype = _i32
+_lib.flce_merge.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.flce_merge.restype = _i32
+_lib.flce_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
+_lib.flce_workspace_bytes.restype = _sz
+_lib.flce_status_string.argtypes = [_i32]
+_lib.flce_status_string.restype = ctypes.c_char_p
+_lib.flce_version.argtypes = []
+_lib.flce_version.restype = _i32
+
+
+class FlcePlan(ctypes.Structure):
+    _fields_ = [
+        ("tile_vocab", ctypes.c_int32), ("tile_tokens", ctypes.c_int32),
+        ("row_blocks", ctypes.c_int32), ("vocab_tiles", ctypes.c_int32),
+        ("chunks", ctypes.c_int32), ("grid", ctypes.c_int32),
+        ("xcd_rows", ctypes.c_int32), ("xcd_chunks", ctypes.c_int32),
+        ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib.flce_get_plan.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(FlcePlan)]
+_lib.flce_get_plan.restype = _i32
+
+EXPORTED = ["flce_forward", "flce_forward_ws", "flce_partials", "flce_merge",
+            "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version"]
+
+
+class FlceError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {flce_status_string(status)} (status {status})")
+        self.status = status
+
+
+def flce_status_string(status: int) -> str:
+    return _lib.flce_status_string(int(status)).decode()
+
+
+def flce_version() -> int:
+    return int(_lib.flce_version())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FLCE_BF16
+    if t.dtype == torch.float32:
+        return FLCE_FP32
+    raise ValueError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _dtype_arg(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    if dtype in (torch.bfloat16, "bf16"):
+        return FLCE_BF16
+    if dtype in (torch.float32, "fp32"):
+        return FLCE_FP32
+    raise ValueError(f"unsupported dtype {dtype!r}")
+
+
+def _stream_ptr(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check_inputs(H, W, targets):
+    for name, t in (("H", H), ("W", W), ("targets", targets)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if H.dim() != 2 or W.dim() != 2 or targets.dim() != 1:
+        raise ValueError("H must be (N, D), W (V, D), targets (N,)")
+    if H.shape[1] != W.shape[1] or targets.shape[0] != H.shape[0]:
+        raise ValueError(f"shape mismatch: H {tuple(H.shape)}, W {tuple(W.shape)}, targets {tuple(targets.shape)}")
+    if H.dtype != W.dtype:
+        raise ValueError("H and W must share a dtype")
+    if targets.dtype != torch.int32:
+        raise ValueError("targets must be int32")
+    if not (H.device == W.device == targets.device):
+        raise ValueError("H, W and targets must be on the same device")
+    return H.shape[0], H.shape[1], W.shape[0], _dtype_code(H)
+
+
+def _out(t, N, device, name):
+    if t is None:
+        return torch.empty(N, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or t.shape != (N,) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 ({N},) tensor on {device}")
+    return t
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
+def flce_workspace_bytes(N: int, D: int, V: int, dtype) -> int:
+    return int(_lib.flce_workspace_bytes(N, D, V, _dtype_arg(dtype)))
+
+
+def flce_get_plan(N: int, D: int, V: int, dtype) -> dict:
+    p = FlcePlan()
+    rc = _lib.flce_get_plan(N, D, V, _dtype_arg(dtype), ctypes.byref(p))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_get_plan")
+    return {name: getattr(p, name) for name, _ in FlcePlan._fields_}
+
+
+def flce_forward(H, W, targets, loss=None, lse=None, stream=None, want_lse=True):
+    """loss (and lse) per token; the workspace is allocated stream-ordered by the library."""
+    N, D, V, dt = _check_inputs(H, W, targets)
+    loss = _out(loss, N, H.device, "loss")
+    if want_lse:
+        lse = _out(lse, N, H.device, "lse")
+    rc = _lib.flce_forward(_ptr(H), _ptr(W), _ptr(targets), N, D, V, dt, _ptr(loss),
+                           _ptr(lse) if want_lse else None, _stream_ptr(stream, H.device))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward")
+    return loss, (lse if want_lse else None)
+
+
+def workspace(N: int, D: int, V: int, dtype, device) -> torch.Tensor:
+    """A device buffer of flce_workspace_bytes for the shape (256-byte aligned)."""
+    nbytes = max(1, flce_workspace_bytes(N, D, V, dtype))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def flce_forward_ws(H, W, targets, ws, loss=None, lse=None, stream=None, want_lse=True):
+    N, D, V, dt = _check_inputs(H, W, targets)
+    loss = _out(loss, N, H.device, "loss")
+    if want_lse:
+        lse = _out(lse, N, H.device, "lse")
+    rc = _lib.flce_forward_ws(_ptr(H), _ptr(W), _ptr(targets), N, D, V, dt, _ptr(loss),
+                              _ptr(lse) if want_lse else None, _ptr(ws), ws.numel() * ws.element_size(),
+                              _stream_ptr(stream, H.device))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward_ws")
+    return loss, (lse if want_lse else None)
+
+
+def flce_partials(H, W, targets, ws, stream=None):
+    N, D, V, dt = _check_inputs(H, W, targets)
+    rc = _lib.flce_partials(_ptr(H), _ptr(W), _ptr(targets), N, D, V, dt, _ptr(ws),
+                            ws.numel() * ws.element_size(), _stream_ptr(stream, H.device))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_partials")
+
+
+def flce_merge(targets, D: int, V: int, dtype, ws, loss=None, lse=None, stream=None):
+    N = targets.shape[0]
+    loss = _out(loss, N, targets.device, "loss")
+    lse = _out(lse, N, targets.device, "lse")
+    rc = _lib.flce_merge(_ptr(targets), N, D, V, _dtype_arg(dtype), _ptr(loss), _ptr(lse), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream_ptr(stream, targets.device))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_merge")
+    return loss, lse
+
+
+def forward(H, W, targets):
+    """Convenience: (loss, lse) on the current stream with a library-managed workspace."""
+    return flce_forward(H, W, targets)

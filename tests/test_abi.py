@@ -1,0 +1,132 @@
+"""The C-ABI library loads and exports every declared symbol; host-side
+argument checks and planning (no GPU, no compute)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def flce():
+    import linear_cross_entropy_amd as m
+    return m
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["flce_forward", "flce_forward_ws", "flce_partials", "flce_merge",
+              "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(flce):
+    lib = ctypes.CDLL(flce.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in flce.h but not exported"
+    assert sorted(flce.EXPORTED) == declared_functions()
+
+
+def test_status_strings(flce):
+    assert flce.flce_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert flce.flce_status_string(code) not in ("", "unknown status")
+    assert flce.flce_status_string(12345) == "unknown status"
+    assert flce.flce_version() >= 100
+
+
+def test_workspace_bytes_is_linear_in_N_not_NxV(flce):
+    N, D, V = 8192, 4096, 151936
+    ws = flce.flce_workspace_bytes(N, D, V, "bf16")
+    plan = flce.flce_get_plan(N, D, V, "bf16")
+    C = plan["chunks"]
+    assert ws >= (2 * C + 1) * N * 4
+    assert ws < (2 * C + 1) * N * 4 + 3 * 256
+    assert ws < 0.01 * N * V * 4          # far below one fp32 logits matrix
+    assert flce.flce_workspace_bytes(0, D, V, "bf16") == 0
+
+
+def test_plan_production_shape(flce):
+    p = flce.flce_get_plan(8192, 4096, 151936, "bf16")
+    assert p["row_blocks"] == math.ceil(8192 / p["tile_tokens"])
+    assert p["vocab_tiles"] == math.ceil(151936 / p["tile_vocab"])
+    assert p["grid"] == p["row_blocks"] * p["chunks"]
+    assert p["grid"] <= 256 or p["grid"] % 256 == 0
+    if p["xcd_rows"]:
+        assert (p["row_blocks"] // p["xcd_rows"]) * (p["chunks"] // p["xcd_chunks"]) == 8
+    assert p["lds_bytes"] <= 160 * 1024
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 1), (3, 72, 31), (2048, 1024, 32000), (4096, 2048, 50257),
+                                   (8192, 8192, 262144), (128, 64, 1024), (1, 4104, 257)])
+def test_plan_covers_every_tile_once(flce, shape):
+    """Chunks partition the vocabulary tiles; every (row block, chunk) has a workgroup."""
+    N, D, V = shape
+    p = flce.flce_get_plan(N, D, V, "bf16")
+    T, C = p["vocab_tiles"], p["chunks"]
+    base, rem = divmod(T, C)
+    starts = [c * base + min(c, rem) for c in range(C)]
+    counts = [base + (c < rem) for c in range(C)]
+    assert starts[0] == 0 and starts[-1] + counts[-1] == T and min(counts) >= 1
+    # the workgroup -> (row block, chunk) map used by the kernel is a bijection
+    seen = set()
+    for b in range(p["grid"]):
+        if p["xcd_rows"]:
+            x, j = b & 7, b >> 3
+            gc = C // p["xcd_chunks"]
+            rb = (x // gc) * p["xcd_rows"] + j // p["xcd_chunks"]
+            ch = (x % gc) * p["xcd_chunks"] + j % p["xcd_chunks"]
+        else:
+            rb, ch = divmod(b, C)
+        assert 0 <= rb < p["row_blocks"] and 0 <= ch < C
+        seen.add((rb, ch))
+    assert len(seen) == p["grid"] == p["row_blocks"] * C
+
+
+def test_invalid_arguments_rejected_before_any_launch(flce):
+    lib = flce._lib
+    buf = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first
+    # bad sizes / dtype
+    assert lib.flce_forward(buf, buf, buf, 4, 0, 10, 0, buf, None, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(buf, buf, buf, 4, 8, 0, 0, buf, None, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(buf, buf, buf, -1, 8, 10, 0, buf, None, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(buf, buf, buf, 4, 8, 10, 7, buf, None, None) == flce.FLCE_ERR_UNSUPPORTED
+    # D * sizeof(elem) must be a multiple of 16
+    assert lib.flce_forward(buf, buf, buf, 4, 12, 10, 0, buf, None, None) == flce.FLCE_ERR_UNSUPPORTED
+    assert lib.flce_forward(buf, buf, buf, 4, 6, 10, 1, buf, None, None) == flce.FLCE_ERR_UNSUPPORTED
+    # null and misaligned pointers
+    assert lib.flce_forward(None, buf, buf, 4, 8, 10, 0, buf, None, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward(buf, buf, buf, 4, 8, 10, 0, None, None, None) == flce.FLCE_ERR_INVALID_ARG
+    odd = ctypes.c_void_p(4096 + 8)
+    assert lib.flce_forward(odd, buf, buf, 4, 8, 10, 0, buf, None, None) == flce.FLCE_ERR_INVALID_ARG
+    # caller workspace too small or misaligned
+    need = flce.flce_workspace_bytes(4, 8, 10, 0)
+    assert lib.flce_forward_ws(buf, buf, buf, 4, 8, 10, 0, buf, None, buf, need - 1, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward_ws(buf, buf, buf, 4, 8, 10, 0, buf, None, odd, need + 64, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_forward_ws(buf, buf, buf, 4, 8, 10, 0, buf, None, None, need, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_partials(buf, buf, buf, 4, 8, 10, 0, buf, need - 1, None) == flce.FLCE_ERR_INVALID_ARG
+    assert lib.flce_merge(buf, 4, 8, 10, 0, None, None, buf, need, None) == flce.FLCE_ERR_INVALID_ARG
+    # N == 0 is a no-op that touches nothing
+    assert lib.flce_forward(None, None, None, 0, 8, 10, 0, None, None, None) == flce.FLCE_OK
+    assert lib.flce_forward_ws(None, None, None, 0, 8, 10, 0, None, None, None, 0, None) == flce.FLCE_OK
+
+
+def test_python_binding_validates_shapes(flce):
+    import torch
+    H = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(10, 8, dtype=torch.bfloat16)
+    y = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        flce.flce_forward(H, W, y)            # CPU tensors are refused
+    with pytest.raises(ValueError):
+        flce._check_inputs(H.cuda() if torch.cuda.is_available() else H, W, y)
