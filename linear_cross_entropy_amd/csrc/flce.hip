@@ -100,9 +100,13 @@ template <> struct Mma<float> {
   }
 };
 
-// XOR swizzle of the eight 16-byte chunks of an LDS row, so that the 32
-// lanes reading one column of chunks for a fragment hit distinct banks.
-__device__ __forceinline__ int swizzle(int row) { return row & 7; }
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row. gfx950's LDS
+// serves a ds_read_b128 16 lanes (256 bytes, all 64 banks) at a time; lanes
+// 0-15 of a fragment read rows r..r+15 at the same logical chunk, and
+// (r >> 1) & 7 sends those 16 reads to 16 distinct 16-byte bank groups
+// (rows r and r+1 differ in bank half, rows 2 apart in chunk). Measured on
+// MI355X: ~247 B/clk/CU with this swizzle, ~127 with (r & 7), ~32 without.
+__device__ __forceinline__ int swizzle(int row) { return (row >> 1) & 7; }
 
 // Combine two partial states (m_a, s_a) and (m_b, s_b) of the online update:
 // M = max(m_a, m_b), S = s_a e^(m_a - M) + s_b e^(m_b - M). A state with
@@ -167,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
   const int row0 = wave * ROWS_PER_WAVE;
   const bool w_wave = row0 < kBV;
   const int region_row0 = w_wave ? row0 : row0 - kBV;
-  const int chunk_off = ((lane & 7) ^ swizzle(lane >> 3)) * 16;  // row0 and 8*i are multiples of 8
+  static_assert(ROWS_PER_WAVE % 16 == 0 && kBV % 16 == 0, "swizzle phase is set by 8*i + lane/8");
   // One buffer resource per operand for the whole chunk: the chunk's W rows
   // (the planner keeps them under 2^31 bytes) and the block's H rows. Rows
   // past V or N and bytes past D fall outside num_records and read as zero.
@@ -176,31 +180,47 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
   const char* region_base = w_wave ? p.W + (size_t)v_chunk0 * p.row_bytes : p.H + (size_t)t0 * p.row_bytes;
   const __amdgpu_buffer_rsrc_t ld_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)region_base, (short)0, region_rows * p.row_bytes, kRsrcWord3);
-  int lane_off[LOADS], lane_row[LOADS];
+  int lane_row[LOADS], chunk_off[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
+    chunk_off[i] = ((lane & 7) ^ swizzle(8 * i + (lane >> 3))) * 16;
     lane_row[i] = region_row0 + 8 * i + (lane >> 3);
-    lane_off[i] = lane_row[i] * p.row_bytes + chunk_off;
   }
-  const int tile_stride = w_wave ? kBV * p.row_bytes : 0;  // H rows stay put across tiles
-
-  int issue_tile = 0, issue_ks = 0;
-  auto issue = [&](int buf) {
-    const int kbyte = issue_ks * kStageRowBytes;
-    const int rows_valid = region_rows - (w_wave ? issue_tile * kBV : 0);
-    const int shift = issue_tile * tile_stride + kbyte;
-    const bool k_ok = kbyte + chunk_off < p.row_bytes;
-    FLCE_LDS char* dst = (FLCE_LDS char*)(smem) + buf * kStageBytes + row0 * kStageRowBytes;
+  // Per tile: each load's byte offset at k = 0, or an out-of-range offset for
+  // rows past the region (an out-of-range base stays out of range after
+  // adding k offsets below 2^31).
+  uint32_t tile_off[LOADS];
+  auto set_tile = [&](int tile) {
+    const int first = w_wave ? tile * kBV : 0;  // H rows stay put across tiles
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const bool ok = k_ok & (lane_row[i] < rows_valid);
-      const uint32_t off = ok ? (uint32_t)(lane_off[i] + shift) : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rsrc, (FLCE_LDS void*)(dst + i * 8 * kStageRowBytes),
-                                               16, off, 0, 0, 0);
+      const int r = first + lane_row[i];
+      tile_off[i] = r < region_rows ? (uint32_t)(r * p.row_bytes + chunk_off[i]) : kOutOfRange;
+    }
+  };
+
+  int issue_tile = 0, issue_ks = 0;
+  set_tile(0);
+  auto issue = [&](int buf) {
+    const int kbyte = issue_ks * kStageRowBytes;
+    FLCE_LDS char* dst = (FLCE_LDS char*)(smem) + buf * kStageBytes + row0 * kStageRowBytes;
+    if (kbyte + kStageRowBytes <= p.row_bytes) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rsrc, (FLCE_LDS void*)(dst + i * 8 * kStageRowBytes), 16,
+                                                 tile_off[i] + kbyte, 0, 0, 0);
+    } else {
+      // last, partial k-stage: chunks past the end of the row read as zero
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const uint32_t off = kbyte + chunk_off[i] < p.row_bytes ? tile_off[i] + kbyte : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rsrc, (FLCE_LDS void*)(dst + i * 8 * kStageRowBytes), 16,
+                                                 off, 0, 0, 0);
+      }
     }
     if (++issue_ks == KS) {
       issue_ks = 0;
-      ++issue_tile;
+      set_tile(++issue_tile);
     }
   };
 
@@ -216,23 +236,51 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
   // ---- per-lane online state for the NB token columns this lane holds.
   // 32x32 MFMA output layout: lane l holds column l%32 and, in register r,
   // row 8*(r/4) + 4*(l/32) + r%4 of the 32x32 tile.
-  float m_run[NB], s_run[NB];
+  float m_run[NB], s_run[NB], zt[NB];
+  bool zhit[NB];
   int ytok[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m_run[nb] = kNegInf;
     s_run[nb] = 0.f;
+    zt[nb] = 0.f;
+    zhit[nb] = false;
     const int tok = t0 + wt * WT + nb * 32 + (lane & 31);
     ytok[nb] = tok < p.N ? p.y[tok] : -1;
   }
 
   f32x16 acc[MB][NB];
+  Frag fa[2][MB], fb[2][NB];  // two fragment sets: one being consumed, one in flight
 
-  if (total > 0) issue(0);
+  auto read_frags = [&](int set, const char* sb, int kb) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      fa[set][mb] = *(const Frag*)(sb + (a_row + mb * 32) * kStageRowBytes + koff[kb]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      fb[set][nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
+  };
+  auto mfmas = [&](int set) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[set][mb], fb[set][nb], acc[mb][nb]);
+  };
+  constexpr int MFMA_PER_KB = MB * NB * (sizeof(T) == 2 ? 1 : 4);  // matrix instructions per k-block
+
+  // ---- main loop over the chunk's stages (tile-major, k-stage minor); stage g
+  // lives in LDS buffer g & 1. After the barrier that publishes stage g (and
+  // retires stage g - 1), a wave reads its first fragments of stage g, issues
+  // the loads of stage g + 1 into the retired buffer, then runs the stage's
+  // four k-blocks with the next k-block's fragment reads spread between the
+  // current k-block's MFMAs.
+  issue(0);
   int ks = 0, tile = 0;
   for (int g = 0; g < total; ++g) {
     FLCE_WAIT_VMCNT(0);          // this wave's loads of stage g have landed in LDS
-    __syncthreads();             // ... and everyone's; stage g-1's buffer is free
+    __syncthreads();             // ... and everyone's; stage g - 1's buffer is free
+    const char* sb = smem + (g & 1) * kStageBytes;
+    read_frags(0, sb, 0);
     if (g + 1 < total) issue((g + 1) & 1);
     if (ks == 0) {
 #pragma unroll
@@ -242,31 +290,31 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
     }
-    const char* sb = smem + (g & 1) * kStageBytes;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      Frag a[MB], b[NB];
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        a[mb] = *(const Frag*)(sb + (a_row + mb * 32) * kStageRowBytes + koff[kb]);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        b[nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(a[mb], b[nb], acc[mb][nb]);
+      if (kb + 1 < 4) read_frags((kb + 1) & 1, sb, kb + 1);
+      mfmas(kb & 1);
     }
-
+#pragma unroll
+    for (int kb = 0; kb < 3; ++kb) {
+#pragma unroll
+      for (int j = 0; j < MB + NB; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_KB - (MB + NB), 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_KB, 0);
     if (++ks < KS) continue;
     ks = 0;
 
-    // ---- epilogue of one vocabulary tile, entirely in registers.
+    // ---- epilogue of one vocabulary tile, entirely in registers
     const int vw = (tile_begin + tile) * kBV + a_row;   // first vocabulary row of this wave
     ++tile;
     if (vw + WV > p.V) {
       // ragged last tile: vocabulary rows >= V are not logits at all
-      const int lim = p.V - vw - 4 * (lane >> 5);
+      int lim = p.V - vw - 4 * (lane >> 5);
+      asm volatile("" : "+v"(lim));  // compared here, not hoisted as per-register lane masks
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -277,18 +325,21 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      // target logit: recorded by the one lane holding (y, token)
+      // target logit: kept by the one lane holding (y, token); written at the end of the chunk
       const int rel = ytok[nb] - vw;
       if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & 1) == (lane >> 5)) {
-        const int want_mb = rel >> 5;
-        const int want_r = ((rel & 31) >> 3) * 4 + (rel & 3);
+        int want = rel;
+        asm volatile("" : "+v"(want));  // likewise
+        const int want_mb = want >> 5;
+        const int want_r = ((want & 31) >> 3) * 4 + (want & 3);
         float val = 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (mb == want_mb && r == want_r) val = acc[mb][nb][r];
-        p.z_target[t0 + wt * WT + nb * 32 + (lane & 31)] = val;
+        zt[nb] = val;
+        zhit[nb] = true;
       }
       // online update: m' = max(m, m_tile), s' = s e^(m - m') + sum_j e^(z_j - m')
       float tmax = kNegInf;
@@ -310,6 +361,11 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
       m_run[nb] = m_new;
     }
   }
+
+  // ---- target logits found in this chunk
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+    if (zhit[nb]) p.z_target[t0 + wt * WT + nb * 32 + (lane & 31)] = zt[nb];
 
   // ---- end of chunk: combine the two half-waves, then the kWavesV waves that
   // share a token range, in a fixed order (deterministic), and write one
