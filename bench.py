@@ -52,7 +52,8 @@ def traffic_from_profile(workload: str):
         return None
     return {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
             "total_bytes": t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"],
-            "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, ROOT)}
+            "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, ROOT),
+            "what": "L2 fetches from the memory fabric (Infinity Cache hits + HBM) and writes, per launch"}
 
 
 def cpu_baseline(H, W, y, w, target_seconds: float, max_rows: int):
@@ -190,7 +191,9 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": traffic,
+            "traffic": traffic["total_bytes"] if traffic else None,
+            "traffic_detail": traffic,
+            "algorithmic_bytes_per_launch": w.N * w.D * 2 + w.V * w.D * 2 + 4 * w.N,
             "algorithmic_flop_per_launch": flops,
             "kernel_ms_avg": avg_ms,
             "kernel_ms_median": kernel_ms_sorted[len(kernel_ms) // 2],
