@@ -26,6 +26,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "flce.h"
 
@@ -52,18 +53,37 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // ------------------------------------------------------------------ tiles
-// One tile configuration: BV vocabulary rows x BT tokens per workgroup,
-// WAVES_V x WAVES_T waves, each wave owning a (BV/WAVES_V) x (BT/WAVES_T)
+// A tile configuration: BV vocabulary rows x BT tokens per workgroup, split
+// over WAVES_V x WAVES_T waves; each wave owns a (BV/WAVES_V) x (BT/WAVES_T)
 // block of 32x32 MFMA tiles. K is staged 128 bytes (64 bf16 / 32 fp32) at a
-// time, double-buffered in LDS.
-constexpr int kBV = 256;
-constexpr int kBT = 256;
-constexpr int kWavesV = 2;
-constexpr int kWavesT = 4;
-constexpr int kThreads = 64 * kWavesV * kWavesT;
+// time, double-buffered in LDS; every wave fills BV/NW W rows and BT/NW H
+// rows of each stage.
 constexpr int kStageRowBytes = 128;
-constexpr int kStageBytes = (kBV + kBT) * kStageRowBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;
+
+template <int BV_, int BT_, int WAVES_V_, int WAVES_T_>
+struct TileCfg {
+  static constexpr int BV = BV_, BT = BT_, WAVES_V = WAVES_V_, WAVES_T = WAVES_T_;
+  static constexpr int NW = WAVES_V * WAVES_T;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WV = BV / WAVES_V;          // vocabulary rows per wave
+  static constexpr int WT = BT / WAVES_T;          // tokens per wave
+  static constexpr int MB = WV / 32;               // 32x32 MFMA tiles along vocabulary
+  static constexpr int NB = WT / 32;               // ... and along tokens
+  static constexpr int WROWS = BV / NW;            // W rows each wave fills per stage
+  static constexpr int HROWS = BT / NW;            // H rows each wave fills per stage
+  static constexpr int WLOADS = WROWS / 8;         // 16-byte loads per lane (8 rows each)
+  static constexpr int HLOADS = HROWS / 8;
+  static constexpr int STAGE_BYTES = (BV + BT) * kStageRowBytes;
+  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  static_assert(WV % 32 == 0 && WT % 32 == 0, "waves own whole MFMA tiles");
+  static_assert(WROWS % 8 == 0 && HROWS % 8 == 0 && BV % 16 == 0, "whole 8-row loads");
+  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
+};
+// 8 waves (two per SIMD), 128 accumulator registers per lane.
+typedef TileCfg<256, 256, 2, 4> Tile8;
+// 8 waves, 160 accumulator registers per lane: 10% fewer bytes staged per
+// FLOP (576 rows per 320x256 tile instead of 512 per 256x256).
+typedef TileCfg<320, 256, 2, 4> Tile4;
 
 struct PartialsArgs {
   const char* H;
@@ -108,31 +128,38 @@ template <> struct Mma<float> {
 // MI355X: ~247 B/clk/CU with this swizzle, ~127 with (r & 7), ~32 without.
 __device__ __forceinline__ int swizzle(int row) { return (row >> 1) & 7; }
 
+// Online-update state (m, s) in base 2: m is the running maximum logit and
+// s = sum_j 2^(z_j log2(e) - off(m)) with off(m) = fl(m * log2(e)), the fp32
+// product, so that e^lse = 2^off(m) * s. Every rescale multiplies by
+// 2^(off(m_old) - off(m_new)), the difference of the same rounded offsets the
+// terms were taken against: an unchanged maximum rescales by exactly 1, and
+// rounding does not compound over the hundreds of tiles a state absorbs.
+// The library is built with -ffp-contract=off (every FMA in this file is an
+// explicit __builtin_fmaf): contracting off2(m_old) - c back into
+// fma(m_old, log2 e, -c) would bring the rounding residual back into every
+// rescale, an error that compounds over the tiles (measured: 1.9e-3 in lse at
+// |lse| = 366 with D = 8192, against 4.6e-4 without it).
+__device__ __forceinline__ float off2(float m) { return m * kLog2e; }
+
 // Combine two partial states (m_a, s_a) and (m_b, s_b) of the online update:
 // M = max(m_a, m_b), S = s_a e^(m_a - M) + s_b e^(m_b - M). A state with
-// m = -inf is empty and contributes nothing.
+// m = -inf is empty (s = 0) and contributes nothing.
 __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
-  const float c = (M == kNegInf) ? 0.f : M * kLog2e;
-  s = s * __builtin_amdgcn_exp2f(__builtin_fmaf(m, kLog2e, -c)) +
-      s2 * __builtin_amdgcn_exp2f(__builtin_fmaf(m2, kLog2e, -c));
+  const float c = (M == kNegInf) ? 0.f : off2(M);
+  s = s * __builtin_amdgcn_exp2f(off2(m) - c) + s2 * __builtin_amdgcn_exp2f(off2(m2) - c);
   m = M;
 }
 
-template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs p) {
+template <typename T, typename C>
+__global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsArgs p) {
   typedef typename Mma<T>::frag Frag;
-  constexpr int NW = kWavesV * kWavesT;
-  constexpr int WV = kBV / kWavesV;          // vocabulary rows per wave
-  constexpr int WT = kBT / kWavesT;          // tokens per wave
-  constexpr int MB = WV / 32;                // 32x32 MFMA tiles along vocab
-  constexpr int NB = WT / 32;                // ... and along tokens
-  constexpr int ROWS_PER_WAVE = (kBV + kBT) / NW;  // LDS rows each wave fills per stage
-  constexpr int LOADS = ROWS_PER_WAVE / 8;         // 16-byte loads per lane per stage
-  static_assert(kBV % ROWS_PER_WAVE == 0, "a wave loads either W or H rows");
-  static_assert(WV % 32 == 0 && WT % 32 == 0, "waves own whole MFMA tiles");
+  constexpr int kBV = C::BV, kBT = C::BT, kWavesV = C::WAVES_V;
+  constexpr int WV = C::WV, WT = C::WT, MB = C::MB, NB = C::NB;
+  constexpr int WLOADS = C::WLOADS, HLOADS = C::HLOADS;
+  constexpr int kStageBytes = C::STAGE_BYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -164,57 +191,74 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
   const int KS = (p.row_bytes + kStageRowBytes - 1) / kStageRowBytes;
   const int total = ntiles * KS;
 
-  // ---- load plan: wave `wave` fills LDS rows [wave*ROWS_PER_WAVE, +ROWS_PER_WAVE)
-  // of each stage; rows < kBV hold W (vocabulary) rows, the rest H (token) rows.
-  // Lane l of load i writes LDS row r = row0 + 8*i + l/8, 16-byte slot l%8,
-  // which holds the row's chunk (l%8) ^ swizzle(r).
-  const int row0 = wave * ROWS_PER_WAVE;
-  const bool w_wave = row0 < kBV;
-  const int region_row0 = w_wave ? row0 : row0 - kBV;
-  static_assert(ROWS_PER_WAVE % 16 == 0 && kBV % 16 == 0, "swizzle phase is set by 8*i + lane/8");
+  // ---- load plan. Each stage holds kBV W rows (LDS rows [0, kBV)) and kBT H
+  // rows (LDS rows [kBV, kBV + kBT)), 128 bytes of K each. Wave w fills W rows
+  // [w*WROWS, +WROWS) and H rows [w*HROWS, +HROWS). Lane l of a load covering
+  // LDS rows r0..r0+7 writes row r0 + l/8, 16-byte slot l%8, which holds the
+  // row's chunk (l%8) ^ swizzle(row).
+  //
   // One buffer resource per operand for the whole chunk: the chunk's W rows
   // (the planner keeps them under 2^31 bytes) and the block's H rows. Rows
   // past V or N and bytes past D fall outside num_records and read as zero.
   const int v_chunk0 = tile_begin * kBV;
-  const int region_rows = w_wave ? min(ntiles * kBV, p.V - v_chunk0) : min(kBT, p.N - t0);
-  const char* region_base = w_wave ? p.W + (size_t)v_chunk0 * p.row_bytes : p.H + (size_t)t0 * p.row_bytes;
-  const __amdgpu_buffer_rsrc_t ld_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)region_base, (short)0, region_rows * p.row_bytes, kRsrcWord3);
-  int lane_row[LOADS], chunk_off[LOADS];
+  const int w_rows = min(ntiles * kBV, p.V - v_chunk0);
+  const int h_rows = min(kBT, p.N - t0);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.W + (size_t)v_chunk0 * p.row_bytes), (short)0, w_rows * p.row_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t h_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.H + (size_t)t0 * p.row_bytes), (short)0, h_rows * p.row_bytes, kRsrcWord3);
+  const int w_row0 = wave * C::WROWS;        // first W row (within the tile) this wave fills
+  const int h_row0 = wave * C::HROWS;        // first H row this wave fills
+  int w_chunk[WLOADS], h_chunk[HLOADS];
 #pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    chunk_off[i] = ((lane & 7) ^ swizzle(8 * i + (lane >> 3))) * 16;
-    lane_row[i] = region_row0 + 8 * i + (lane >> 3);
-  }
-  // Per tile: each load's byte offset at k = 0, or an out-of-range offset for
-  // rows past the region (an out-of-range base stays out of range after
-  // adding k offsets below 2^31).
-  uint32_t tile_off[LOADS];
+  for (int i = 0; i < WLOADS; ++i) w_chunk[i] = ((lane & 7) ^ swizzle(w_row0 + 8 * i + (lane >> 3))) * 16;
+#pragma unroll
+  for (int i = 0; i < HLOADS; ++i) h_chunk[i] = ((lane & 7) ^ swizzle(kBV + h_row0 + 8 * i + (lane >> 3))) * 16;
+  // Byte offset of each load at k = 0, or an out-of-range offset for rows past
+  // the region (an out-of-range base stays out of range after adding k < 2^31).
+  uint32_t w_off[WLOADS], h_off[HLOADS];
   auto set_tile = [&](int tile) {
-    const int first = w_wave ? tile * kBV : 0;  // H rows stay put across tiles
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int r = first + lane_row[i];
-      tile_off[i] = r < region_rows ? (uint32_t)(r * p.row_bytes + chunk_off[i]) : kOutOfRange;
+    for (int i = 0; i < WLOADS; ++i) {
+      const int r = tile * kBV + w_row0 + 8 * i + (lane >> 3);
+      w_off[i] = r < w_rows ? (uint32_t)(r * p.row_bytes + w_chunk[i]) : kOutOfRange;
     }
   };
+#pragma unroll
+  for (int i = 0; i < HLOADS; ++i) {
+    const int r = h_row0 + 8 * i + (lane >> 3);
+    h_off[i] = r < h_rows ? (uint32_t)(r * p.row_bytes + h_chunk[i]) : kOutOfRange;
+  }
 
   int issue_tile = 0, issue_ks = 0;
   set_tile(0);
+  // (offsets are cast explicitly: without it the host-side instantiation of
+  // this template drops the kernel's launch stub)
   auto issue = [&](int buf) {
     const int kbyte = issue_ks * kStageRowBytes;
-    FLCE_LDS char* dst = (FLCE_LDS char*)(smem) + buf * kStageBytes + row0 * kStageRowBytes;
+    FLCE_LDS char* wdst = (FLCE_LDS char*)(smem) + buf * kStageBytes + w_row0 * kStageRowBytes;
+    FLCE_LDS char* hdst = (FLCE_LDS char*)(smem) + buf * kStageBytes + (kBV + h_row0) * kStageRowBytes;
     if (kbyte + kStageRowBytes <= p.row_bytes) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rsrc, (FLCE_LDS void*)(dst + i * 8 * kStageRowBytes), 16,
-                                                 tile_off[i] + kbyte, 0, 0, 0);
+      for (int i = 0; i < WLOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (FLCE_LDS void*)(wdst + i * 8 * kStageRowBytes), 16,
+                                                 (uint32_t)(w_off[i] + kbyte), 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < HLOADS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(h_rsrc, (FLCE_LDS void*)(hdst + i * 8 * kStageRowBytes), 16,
+                                                 (uint32_t)(h_off[i] + kbyte), 0, 0, 0);
     } else {
       // last, partial k-stage: chunks past the end of the row read as zero
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const uint32_t off = kbyte + chunk_off[i] < p.row_bytes ? tile_off[i] + kbyte : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ld_rsrc, (FLCE_LDS void*)(dst + i * 8 * kStageRowBytes), 16,
+      for (int i = 0; i < WLOADS; ++i) {
+        const uint32_t off = kbyte + w_chunk[i] < p.row_bytes ? w_off[i] + kbyte : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (FLCE_LDS void*)(wdst + i * 8 * kStageRowBytes), 16,
+                                                 off, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < HLOADS; ++i) {
+        const uint32_t off = kbyte + h_chunk[i] < p.row_bytes ? h_off[i] + kbyte : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(h_rsrc, (FLCE_LDS void*)(hdst + i * 8 * kStageRowBytes), 16,
                                                  off, 0, 0, 0);
       }
     }
@@ -348,7 +392,7 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
       const float m_new = fmaxf(m_run[nb], tmax);
-      const float c = (m_new == kNegInf) ? 0.f : m_new * kLog2e;
+      const float c = (m_new == kNegInf) ? 0.f : off2(m_new);
       float s0 = 0.f, s1 = 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -357,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
           s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], kLog2e, -c));
           s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r + 1], kLog2e, -c));
         }
-      s_run[nb] = s_run[nb] * __builtin_amdgcn_exp2f(__builtin_fmaf(m_run[nb], kLog2e, -c)) + (s0 + s1);
+      s_run[nb] = s_run[nb] * __builtin_amdgcn_exp2f(off2(m_run[nb]) - c) + (s0 + s1);
       m_run[nb] = m_new;
     }
   }
@@ -403,8 +447,10 @@ __global__ __launch_bounds__(kThreads, 1) void flce_partials_kernel(PartialsArgs
   }
 }
 
-// Merge: one thread per token. M = max_c m_c, S = sum_c s_c e^(m_c - M),
-// lse = M + ln S, loss = lse - z_y (NaN when y is not in [0, V)).
+// Merge: one thread per token, in double precision (a handful of operations
+// per row). With off(m) = fl(m log2 e) as in the partials kernel,
+// C = max_c off(m_c), S = sum_c s_c 2^(off(m_c) - C), lse = (C + log2 S) ln 2
+// and loss = lse - z_y (NaN when y is not in [0, V)).
 __global__ __launch_bounds__(256) void flce_merge_kernel(const float* __restrict__ part_m,
                                                          const float* __restrict__ part_s,
                                                          const float* __restrict__ z_target,
@@ -413,31 +459,51 @@ __global__ __launch_bounds__(256) void flce_merge_kernel(const float* __restrict
                                                          float* __restrict__ lse) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
-  float M = kNegInf;
-  for (int c = 0; c < chunks; ++c) M = fmaxf(M, part_m[(size_t)c * N + i]);
-  float S = 0.f;
+  double C = -__builtin_inf();
+  for (int c = 0; c < chunks; ++c) C = fmax(C, (double)off2(part_m[(size_t)c * N + i]));
+  double S = 0.0;
   for (int c = 0; c < chunks; ++c) {
-    const float m = part_m[(size_t)c * N + i];
-    const float w = (m == kNegInf) ? 0.f : expf(m - M);
-    S += part_s[(size_t)c * N + i] * w;
+    const double o = (double)off2(part_m[(size_t)c * N + i]);
+    const double w = (o == -__builtin_inf()) ? 0.0 : exp2(o - C);
+    S += (double)part_s[(size_t)c * N + i] * w;
   }
-  const float l = M + logf(S);
-  if (lse) lse[i] = l;
+  const double l = (C + log2(S)) * 0.69314718055994530942;
+  if (lse) lse[i] = (float)l;
   const int t = y[i];
-  loss[i] = (t >= 0 && t < V) ? l - z_target[i] : __builtin_nanf("");
+  loss[i] = (t >= 0 && t < V) ? (float)(l - (double)z_target[i]) : __builtin_nanf("");
 }
 
 // ------------------------------------------------------------------ host side
 constexpr int kSlots = 256;       // workgroups resident at once: one per CU
 constexpr size_t kAlign = 256;
 
+enum TileId { kTile8 = 0, kTile4 = 1 };
+
 struct Plan {
-  int N, V, row_bytes, dtype;
+  int N, V, row_bytes, dtype, tile;
+  int BV, BT, threads, lds_bytes;
   int row_blocks, vocab_tiles, chunks, grid, xcd_rows, xcd_chunks;
   size_t off_m, off_s, off_z, ws_bytes;
 };
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Tile configuration for a shape: the 4-wave 384x256 tile stages fewer bytes
+// per FLOP and is used for bf16 whenever the shape is large enough to fill
+// the machine with it; fp32 and small problems use the 8-wave 256x256 tile.
+// FLCE_TILE=8 or FLCE_TILE=4 in the environment forces one configuration (for
+// tests and tuning; both compute the same result).
+int choose_tile(int64_t N, int64_t V, int dtype) {
+  if (dtype != FLCE_BF16) return kTile8;
+  static const int forced = [] {
+    const char* e = getenv("FLCE_TILE");
+    return e ? atoi(e) : 0;
+  }();
+  if (forced == 8) return kTile8;
+  if (forced == 4) return kTile4;
+  const int64_t tiles4 = ((N + Tile4::BT - 1) / Tile4::BT) * ((V + Tile4::BV - 1) / Tile4::BV);
+  return tiles4 >= 4 * kSlots ? kTile4 : kTile8;
+}
 
 int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl) {
   if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
@@ -445,6 +511,13 @@ int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl) {
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   const int64_t rb = D * es;
   if (rb % 16 != 0) return FLCE_ERR_UNSUPPORTED;
+  pl->tile = choose_tile(N, V, dtype);
+  const int kBV = pl->tile == kTile4 ? Tile4::BV : Tile8::BV;
+  const int kBT = pl->tile == kTile4 ? Tile4::BT : Tile8::BT;
+  pl->BV = kBV;
+  pl->BT = kBT;
+  pl->threads = pl->tile == kTile4 ? Tile4::THREADS : Tile8::THREADS;
+  pl->lds_bytes = pl->tile == kTile4 ? Tile4::LDS_BYTES : Tile8::LDS_BYTES;
   // 32-bit offsets inside one tile's buffer resource, int32 indices elsewhere
   if ((int64_t)kBV * rb >= (int64_t(1) << 31) || N > INT32_MAX / 2 || V > INT32_MAX - kBV)
     return FLCE_ERR_UNSUPPORTED;
@@ -532,10 +605,12 @@ int launch_partials(const Plan& pl, const void* H, const void* W, const int32_t*
   a.chunks = pl.chunks;
   a.xcd_rows = pl.xcd_rows;
   a.xcd_chunks = pl.xcd_chunks;
-  if (pl.dtype == FLCE_BF16)
-    hipLaunchKernelGGL(flce_partials_kernel<__bf16>, dim3(pl.grid), dim3(kThreads), 0, stream, a);
+  if (pl.dtype == FLCE_BF16 && pl.tile == kTile4)
+    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile4>), dim3(pl.grid), dim3(Tile4::THREADS), 0, stream, a);
+  else if (pl.dtype == FLCE_BF16)
+    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile8>), dim3(pl.grid), dim3(Tile8::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL(flce_partials_kernel<float>, dim3(pl.grid), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((flce_partials_kernel<float, Tile8>), dim3(pl.grid), dim3(Tile8::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -571,16 +646,16 @@ int flce_get_plan(int64_t N, int64_t D, int64_t V, int dtype, flce_plan_t* out) 
   Plan pl;
   const int rc = make_plan(N, D, V, dtype, &pl);
   if (rc != FLCE_OK) return rc;
-  out->tile_vocab = kBV;
-  out->tile_tokens = kBT;
+  out->tile_vocab = pl.BV;
+  out->tile_tokens = pl.BT;
   out->row_blocks = pl.row_blocks;
   out->vocab_tiles = pl.vocab_tiles;
   out->chunks = pl.chunks;
   out->grid = N > 0 ? pl.grid : 0;
   out->xcd_rows = pl.xcd_rows;
   out->xcd_chunks = pl.xcd_chunks;
-  out->threads = kThreads;
-  out->lds_bytes = kLdsBytes;
+  out->threads = pl.threads;
+  out->lds_bytes = pl.lds_bytes;
   out->workspace_bytes = N > 0 ? pl.ws_bytes : 0;
   return FLCE_OK;
 }

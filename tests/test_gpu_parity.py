@@ -41,10 +41,16 @@ def _log(msg):
     ("stress_bf16", 48),
 ])
 def test_workload_parity(name, sample):
+    """Every row where the oracle is cheap; otherwise a seeded sample plus the 32
+    rows with the largest lse (largest logits, so the largest fp32 rounding)."""
     w = workloads.WORKLOADS[name]
     _log(f"[parity] {w.describe()} sample={sample}")
     H, W, y = workloads.make(w, DEV)
-    rows = None if sample is None else workloads.subset_rows(w.N, sample).numpy()
+    rows = None
+    if sample is not None:
+        _, lse_gpu = gpu_forward(H, W, y)
+        top = np.argsort(lse_gpu)[-32:]
+        rows = np.union1d(workloads.subset_rows(w.N, sample).numpy(), top)
     loss, lse, err = parity(H, W, y, rows=rows, what=name)
     assert np.isfinite(loss).all() and np.isfinite(lse).all()
     assert (loss >= -2e-3).all(), "loss below 0 beyond rounding"
@@ -64,6 +70,7 @@ EDGE = [
     (64, 1024, 32001, "bf16"),
     (64, 1024, 31999, "bf16"),
     (40, 256, 50257, "bf16"),
+    (1000, 136, 100003, "bf16"),   # large enough for the 320x256 tile: ragged rows, vocabulary and K
     (1, 4, 1, "fp32"),
     (5, 36, 300, "fp32"),
     (257, 128, 1025, "fp32"),
@@ -111,6 +118,33 @@ def test_out_of_range_targets_give_nan_loss():
     assert np.isnan(loss[:4]).all()
     assert np.isfinite(lse).all() and np.isfinite(loss[4:]).all()
     parity(H, W, y, what="out-of-range targets")
+
+
+def test_large_logit_held_over_many_tiles():
+    """A logit near 1000 in the first tile of every vocabulary chunk, then ~100
+    tiles whose maximum stays below it, so each of those tiles must rescale the
+    running sum by exactly 1. (A rescale that re-derives the base-2 offset with
+    an extra rounding drifts by up to 6e-5 per tile at this magnitude, several
+    1e-3 in lse over a chunk.)"""
+    import linear_cross_entropy_amd as flce
+    N, D, V = 8192, 64, 262144
+    plan = flce.flce_get_plan(N, D, V, "bf16")
+    T, C, BV = plan["vocab_tiles"], plan["chunks"], plan["tile_vocab"]
+    assert T // C >= 64, "the shape must give long chunks"
+    base, rem = divmod(T, C)
+    starts = [(c * base + min(c, rem)) * BV for c in range(C)]
+    g = torch.Generator().manual_seed(17)
+    H = torch.randn(N, D, generator=g)
+    H[:, 0] = 1000.0 + 8.0 * (torch.arange(N) % 16)      # exact in bf16 (spacing 8 at 1000)
+    W = torch.randn(V, D, generator=g) * 0.3
+    W[:, 0] = 0.0
+    W[starts, 0] = 1.0                                    # the first row of every chunk carries the large logit
+    H, W = H.to(torch.bfloat16).to(DEV), W.to(torch.bfloat16).to(DEV)
+    y = torch.randint(0, V, (N,), generator=g, dtype=torch.int32).to(DEV)
+    rows = workloads.subset_rows(N, 256, seed=5).numpy()
+    _, lse, err = parity(H, W, y, rows=rows, what="large logit over many tiles")
+    assert (lse > 990.0).all()
+    _log(f"[parity] large logit over many tiles: max |d| = {err:.3e}")
 
 
 def test_zero_weights_give_log_V():
