@@ -79,11 +79,15 @@ struct TileCfg {
   static_assert(WROWS % 8 == 0 && HROWS % 8 == 0 && BV % 16 == 0, "whole 8-row loads");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
 };
-// 8 waves (two per SIMD), 128 accumulator registers per lane.
-typedef TileCfg<256, 256, 2, 4> Tile8;
-// 8 waves, 160 accumulator registers per lane: 10% fewer bytes staged per
-// FLOP (576 rows per 320x256 tile instead of 512 per 256x256).
-typedef TileCfg<320, 256, 2, 4> Tile4;
+// All three run 8 waves (two per SIMD). Staged bytes per FLOP fall with the
+// tile, (BV + BT) / (BV * BT): 256x256 stages 512 rows per 65536 logits,
+// 320x256 576 per 81920 (-10%), 384x256 640 per 98304 (-17%). The staging
+// path (global -> LDS) is what bounds the kernel at large shapes, so the
+// largest tile that fills the machine wins; 384x256 takes the whole 160 KB
+// of LDS and 192 accumulator registers per lane.
+typedef TileCfg<256, 256, 2, 4> Tile256;
+typedef TileCfg<320, 256, 2, 4> Tile320;
+typedef TileCfg<384, 256, 2, 4> Tile384;
 
 struct PartialsArgs {
   const char* H;
@@ -294,23 +298,22 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
   }
 
   f32x16 acc[MB][NB];
-  Frag fa[2][MB], fb[2][NB];  // two fragment sets: one being consumed, one in flight
-
-  auto read_frags = [&](int set, const char* sb, int kb) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-      fa[set][mb] = *(const Frag*)(sb + (a_row + mb * 32) * kStageRowBytes + koff[kb]);
+  // Fragments: the NB H fragments of the current k-block and of the next one
+  // (two sets), and a rolling window of kASlots W fragments. W fragment q of
+  // a stage (q = kb*MB + mb) lives in slot q % kASlots; once the MFMAs that
+  // use it have issued, the slot receives fragment q + kASlots.
+  constexpr int kASlots = 3;
+  constexpr int QN = 4 * MB;  // W fragments per stage
+  Frag fa[kASlots], fb[2][NB];
+  auto read_a = [&](const char* sb, int q) {
+    fa[q % kASlots] = *(const Frag*)(sb + (a_row + (q % MB) * 32) * kStageRowBytes + koff[q / MB]);
+  };
+  auto read_b = [&](const char* sb, int kb) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      fb[set][nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
+      fb[kb & 1][nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
   };
-  auto mfmas = [&](int set) {
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[set][mb], fb[set][nb], acc[mb][nb]);
-  };
-  constexpr int MFMA_PER_KB = MB * NB * (sizeof(T) == 2 ? 1 : 4);  // matrix instructions per k-block
+  constexpr int STEPS = NB * (sizeof(T) == 2 ? 1 : 4);  // matrix instructions per W fragment
 
   // ---- main loop over the chunk's stages (tile-major, k-stage minor); stage g
   // lives in LDS buffer g & 1. After the barrier that publishes stage g (and
@@ -324,7 +327,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
     FLCE_WAIT_VMCNT(0);          // this wave's loads of stage g have landed in LDS
     __syncthreads();             // ... and everyone's; stage g - 1's buffer is free
     const char* sb = smem + (g & 1) * kStageBytes;
-    read_frags(0, sb, 0);
+#pragma unroll
+    for (int q = 0; q < kASlots; ++q) read_a(sb, q);
+    read_b(sb, 0);
     if (g + 1 < total) issue((g + 1) & 1);
     if (ks == 0) {
 #pragma unroll
@@ -335,20 +340,27 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
           for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
     }
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if (kb + 1 < 4) read_frags((kb + 1) & 1, sb, kb + 1);
-      mfmas(kb & 1);
+    for (int q = 0; q < QN; ++q) {
+      const int kb = q / MB, mb = q % MB;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb & 1][nb], acc[mb][nb]);
+      if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
+      if (q + kASlots < QN) read_a(sb, q + kASlots);
     }
+    // keep that order: each W fragment's matrix instructions, then the reads
+    // its slot (and, at a k-block's start, the idle H set) can take
 #pragma unroll
-    for (int kb = 0; kb < 3; ++kb) {
-#pragma unroll
-      for (int j = 0; j < MB + NB; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    for (int q = 0; q < QN; ++q) {
+      const int kb = q / MB, mb = q % MB;
+      if (mb == 0 && kb + 1 < 4) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);          // next k-block's H fragments
+        __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_KB - (MB + NB), 0);
+      if (q + kASlots < QN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one W fragment
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_KB, 0);
     if (++ks < KS) continue;
     ks = 0;
 
@@ -477,7 +489,7 @@ __global__ __launch_bounds__(256) void flce_merge_kernel(const float* __restrict
 constexpr int kSlots = 256;       // workgroups resident at once: one per CU
 constexpr size_t kAlign = 256;
 
-enum TileId { kTile8 = 0, kTile4 = 1 };
+enum TileId { kTile256 = 0, kTile320 = 1, kTile384 = 2 };
 
 struct Plan {
   int N, V, row_bytes, dtype, tile;
@@ -488,21 +500,65 @@ struct Plan {
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Tile configuration for a shape: the 4-wave 384x256 tile stages fewer bytes
-// per FLOP and is used for bf16 whenever the shape is large enough to fill
-// the machine with it; fp32 and small problems use the 8-wave 256x256 tile.
-// FLCE_TILE=8 or FLCE_TILE=4 in the environment forces one configuration (for
-// tests and tuning; both compute the same result).
-int choose_tile(int64_t N, int64_t V, int dtype) {
-  if (dtype != FLCE_BF16) return kTile8;
+struct TileInfo {
+  int BV, BT, threads, lds_bytes;
+  int cost_per_logit;  // relative time per logit at large shapes (x1000), measured on MI355X
+};
+template <typename C>
+constexpr TileInfo tile_info(int cost) {
+  return TileInfo{C::BV, C::BT, C::THREADS, C::LDS_BYTES, cost};
+}
+// Per-logit costs from the production shape (N=8192, D=4096, V=151936):
+// 8.60, 8.14 and 7.80 ms for the same work with 256-, 320- and 384-row tiles.
+constexpr TileInfo kTiles[3] = {tile_info<Tile256>(1106), tile_info<Tile320>(1044), tile_info<Tile384>(1000)};
+
+// Chunks per row block for a tile: minimise the makespan in tile-times,
+// ceil(row_blocks*c / slots) * ceil(vocab_tiles / c); ties go to fewer chunks.
+// Returns 0 when no chunk count keeps a chunk's W rows under 2^31 bytes.
+int best_chunks(int64_t row_blocks, int64_t vocab_tiles, int64_t BV, int64_t row_bytes, int64_t* makespan) {
+  int best_c = 0;
+  int64_t best_cost = INT64_MAX;
+  const int64_t RB = row_blocks > 0 ? row_blocks : 1;
+  for (int64_t c = 1; c <= vocab_tiles; ++c) {
+    const int64_t rounds = (RB * c + kSlots - 1) / kSlots;
+    const int64_t per = (vocab_tiles + c - 1) / c;
+    if (per * BV * row_bytes >= (int64_t(1) << 31)) continue;  // one buffer resource per chunk
+    const int64_t cost = rounds * per;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best_c = (int)c;
+    }
+  }
+  *makespan = best_cost;
+  return best_c;
+}
+
+// Tile configuration for a shape: fp32 always uses 256x256; for bf16 the
+// tile whose makespan (tile-times x logits per tile x cost per logit) is
+// smallest. FLCE_TILE=256, 320 or 384 in the environment forces a bf16
+// configuration (for tests and tuning; every configuration computes the same
+// result).
+int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype) {
+  if (dtype != FLCE_BF16) return kTile256;
   static const int forced = [] {
     const char* e = getenv("FLCE_TILE");
-    return e ? atoi(e) : 0;
+    const int v = e ? atoi(e) : 0;
+    return v == 256 ? kTile256 : v == 320 ? kTile320 : v == 384 ? kTile384 : -1;
   }();
-  if (forced == 8) return kTile8;
-  if (forced == 4) return kTile4;
-  const int64_t tiles4 = ((N + Tile4::BT - 1) / Tile4::BT) * ((V + Tile4::BV - 1) / Tile4::BV);
-  return tiles4 >= 4 * kSlots ? kTile4 : kTile8;
+  if (forced >= 0) return forced;
+  int best = kTile256;
+  double best_t = 0;
+  for (int t = kTile256; t <= kTile384; ++t) {
+    const TileInfo& ti = kTiles[t];
+    int64_t makespan = 0;
+    if (best_chunks((N + ti.BT - 1) / ti.BT, (V + ti.BV - 1) / ti.BV, ti.BV, row_bytes, &makespan) == 0) continue;
+    const double est = (double)makespan * ti.BV * ti.BT * ti.cost_per_logit;
+    if (t == kTile256 || est < best_t) {
+      best = t;
+      best_t = est;
+    }
+  }
+  return best;
 }
 
 int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl) {
@@ -511,13 +567,13 @@ int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl) {
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   const int64_t rb = D * es;
   if (rb % 16 != 0) return FLCE_ERR_UNSUPPORTED;
-  pl->tile = choose_tile(N, V, dtype);
-  const int kBV = pl->tile == kTile4 ? Tile4::BV : Tile8::BV;
-  const int kBT = pl->tile == kTile4 ? Tile4::BT : Tile8::BT;
+  pl->tile = choose_tile(N, V, rb, dtype);
+  const TileInfo& ti = kTiles[pl->tile];
+  const int kBV = ti.BV, kBT = ti.BT;
   pl->BV = kBV;
   pl->BT = kBT;
-  pl->threads = pl->tile == kTile4 ? Tile4::THREADS : Tile8::THREADS;
-  pl->lds_bytes = pl->tile == kTile4 ? Tile4::LDS_BYTES : Tile8::LDS_BYTES;
+  pl->threads = ti.threads;
+  pl->lds_bytes = ti.lds_bytes;
   // 32-bit offsets inside one tile's buffer resource, int32 indices elsewhere
   if ((int64_t)kBV * rb >= (int64_t(1) << 31) || N > INT32_MAX / 2 || V > INT32_MAX - kBV)
     return FLCE_ERR_UNSUPPORTED;
@@ -527,22 +583,10 @@ int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl) {
   pl->dtype = dtype;
   pl->row_blocks = (int)((N + kBT - 1) / kBT);
   pl->vocab_tiles = (int)((V + kBV - 1) / kBV);
-  // chunks per row block: minimise the makespan in tile-times,
-  // ceil(row_blocks*c / slots) * ceil(vocab_tiles / c); ties go to fewer chunks.
-  int best_c = 0;
-  int64_t best_cost = INT64_MAX;
-  const int RB = pl->row_blocks > 0 ? pl->row_blocks : 1;
-  for (int c = 1; c <= pl->vocab_tiles; ++c) {
-    const int64_t rounds = ((int64_t)RB * c + kSlots - 1) / kSlots;
-    const int64_t per = (pl->vocab_tiles + c - 1) / c;
-    if (per * kBV * rb >= (int64_t(1) << 31)) continue;  // one buffer resource per chunk
-    const int64_t cost = rounds * per;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best_c = c;
-    }
-  }
+  int64_t makespan = 0;
+  const int best_c = best_chunks(pl->row_blocks, pl->vocab_tiles, kBV, rb, &makespan);
   if (best_c == 0) return FLCE_ERR_UNSUPPORTED;
+  const int RB = pl->row_blocks > 0 ? pl->row_blocks : 1;
   pl->chunks = best_c;
   pl->grid = RB * best_c;
   // XCD groups: 8 equal blocks of the (row block, chunk) grid, each
@@ -605,12 +649,14 @@ int launch_partials(const Plan& pl, const void* H, const void* W, const int32_t*
   a.chunks = pl.chunks;
   a.xcd_rows = pl.xcd_rows;
   a.xcd_chunks = pl.xcd_chunks;
-  if (pl.dtype == FLCE_BF16 && pl.tile == kTile4)
-    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile4>), dim3(pl.grid), dim3(Tile4::THREADS), 0, stream, a);
-  else if (pl.dtype == FLCE_BF16)
-    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile8>), dim3(pl.grid), dim3(Tile8::THREADS), 0, stream, a);
+  if (pl.dtype == FLCE_FP32)
+    hipLaunchKernelGGL((flce_partials_kernel<float, Tile256>), dim3(pl.grid), dim3(Tile256::THREADS), 0, stream, a);
+  else if (pl.tile == kTile384)
+    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile384>), dim3(pl.grid), dim3(Tile384::THREADS), 0, stream, a);
+  else if (pl.tile == kTile320)
+    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile320>), dim3(pl.grid), dim3(Tile320::THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL((flce_partials_kernel<float, Tile8>), dim3(pl.grid), dim3(Tile8::THREADS), 0, stream, a);
+    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile256>), dim3(pl.grid), dim3(Tile256::THREADS), 0, stream, a);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

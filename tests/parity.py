@@ -52,3 +52,31 @@ def parity(H, W, y, rows=None, what="", Hc=None, Wc=None):
     e1 = check_close(lse[sel], rs, H.dtype, f"{what} lse")
     e2 = check_close(loss[sel], rl, H.dtype, f"{what} loss")
     return loss, lse, max(e1, e2)
+
+
+# Edge shapes for the GPU parity grid (N, D, V, dtype): degenerate sizes,
+# ragged rows, vocabulary and K, and shapes large enough that the planner
+# picks each tile configuration (a host-side test checks that all of them are
+# exercised).
+EDGE = [
+    (1, 8, 1, "bf16"),
+    (3, 8, 2, "bf16"),
+    (3, 72, 31, "bf16"),
+    (257, 72, 255, "bf16"),
+    (257, 64, 256, "bf16"),
+    (3, 64, 257, "bf16"),
+    (300, 4104, 513, "bf16"),
+    (64, 1024, 32001, "bf16"),
+    (64, 1024, 31999, "bf16"),
+    (40, 256, 50257, "bf16"),
+    (1000, 136, 100003, "bf16"),   # 320x256 tile: ragged rows, vocabulary and K
+    (4096, 64, 65536, "bf16"),     # 384x256 tile, one k-stage per tile, ragged vocabulary
+    (3000, 64, 120000, "bf16"),    # 384x256 tile without the XCD remap, ragged rows and vocabulary
+    (1, 4, 1, "fp32"),
+    (5, 36, 300, "fp32"),
+    (257, 128, 1025, "fp32"),
+]
+
+# (N, D, V) for the tile- and chunk-boundary target test, one per tile size
+BOUNDARY_SHAPES = [(512, 256, 50257), (1024, 64, 151936), (4096, 64, 65536)]
+

@@ -93,6 +93,24 @@ def test_plan_covers_every_tile_once(flce, shape):
     assert len(seen) == p["grid"] == p["row_blocks"] * C
 
 
+def test_gpu_parity_shapes_exercise_every_tile(flce):
+    """The GPU parity grid reaches every bf16 tile configuration the planner
+    can choose, with ragged vocabulary in each."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from parity import BOUNDARY_SHAPES, EDGE
+    import workloads
+    shapes = [(N, D, V) for N, D, V, dt in EDGE if dt == "bf16"] + list(BOUNDARY_SHAPES)
+    shapes += [(w.N, w.D, w.V) for w in workloads.WORKLOADS.values() if w.dtype == "bf16"]
+    ragged = {}
+    for N, D, V in shapes:
+        p = flce.flce_get_plan(N, D, V, "bf16")
+        ragged.setdefault(p["tile_vocab"], False)
+        ragged[p["tile_vocab"]] |= V % p["tile_vocab"] != 0
+    assert set(ragged) == {256, 320, 384}
+    assert all(ragged.values())
+
+
 def test_invalid_arguments_rejected_before_any_launch(flce):
     lib = flce._lib
     buf = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from parity import check_close, gpu_forward, parity
+from parity import BOUNDARY_SHAPES, EDGE, check_close, gpu_forward, parity
 
 pytestmark = pytest.mark.gpu
 
@@ -58,25 +58,6 @@ def test_workload_parity(name, sample):
 
 
 # ------------------------------------------------------------------ edge grid
-EDGE = [
-    # (N, D, V, dtype)
-    (1, 8, 1, "bf16"),
-    (3, 8, 2, "bf16"),
-    (3, 72, 31, "bf16"),
-    (257, 72, 255, "bf16"),
-    (257, 64, 256, "bf16"),
-    (3, 64, 257, "bf16"),
-    (300, 4104, 513, "bf16"),
-    (64, 1024, 32001, "bf16"),
-    (64, 1024, 31999, "bf16"),
-    (40, 256, 50257, "bf16"),
-    (1000, 136, 100003, "bf16"),   # large enough for the 320x256 tile: ragged rows, vocabulary and K
-    (1, 4, 1, "fp32"),
-    (5, 36, 300, "fp32"),
-    (257, 128, 1025, "fp32"),
-]
-
-
 @pytest.mark.parametrize("N,D,V,dt", EDGE, ids=lambda v: str(v))
 def test_edge_shapes(N, D, V, dt):
     std = 1.0 if dt == "bf16" else 0.5
@@ -86,9 +67,9 @@ def test_edge_shapes(N, D, V, dt):
     parity(H, W, y, what=f"edge N={N} D={D} V={V} {dt}")
 
 
-def test_targets_on_tile_and_chunk_boundaries():
+@pytest.mark.parametrize("N,D,V", BOUNDARY_SHAPES, ids=lambda v: str(v))
+def test_targets_on_tile_and_chunk_boundaries(N, D, V):
     """Targets at 0, V-1 and either side of every tile and chunk boundary."""
-    N, D, V = 512, 256, 50257
     import linear_cross_entropy_amd as flce
     plan = flce.flce_get_plan(N, D, V, "bf16")
     BV, T, C = plan["tile_vocab"], plan["vocab_tiles"], plan["chunks"]
@@ -104,7 +85,8 @@ def test_targets_on_tile_and_chunk_boundaries():
     marks = sorted(m for m in marks if 0 <= m < V)
     H, W, _ = workloads.make_custom(N, D, V, "bf16", seed=11, device=DEV)
     y = torch.tensor([marks[i % len(marks)] for i in range(N)], dtype=torch.int32, device=DEV)
-    parity(H, W, y, what="boundary targets")
+    _log(f"[boundary] N={N} D={D} V={V} tile={BV} chunks={C}")
+    parity(H, W, y, what=f"boundary targets N={N} D={D} V={V}")
 
 
 def test_out_of_range_targets_give_nan_loss():
