@@ -35,9 +35,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_flce_partials_prod_bf16.j
 KERNEL_SRC = os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "flce.hip")
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_sha(path: str = KERNEL_SRC) -> str:
+    """Hash of the kernel source with comments and whitespace removed, so that
+    counters stay attached to the code they were taken on across comment edits."""
+    import re
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str):

@@ -1,8 +1,8 @@
 /*
  * flce.h -- fused linear cross-entropy forward on AMD Instinct MI355X (gfx950).
  *
- * The operation is the one defined on the page "A fused forward kernel for
- * linear cross-entropy on Apple GPUs" (section 1): for hidden states H
+ * The operation is the one defined on the page "Een gefuseerde forward-kernel
+ * voor lineaire cross-entropy op Apple-GPU's" (section 1): for hidden states H
  * (N x D) and an output projection W (V x D) the logits are Z = H W^T, and
  * for each token i with target y_i
  *

@@ -14,8 +14,8 @@ device memory and the stream. The functions keep the C names:
     flce_status_string(status) -> str
     flce_version() -> int
 
-The operation (page "A fused forward kernel for linear cross-entropy on
-Apple GPUs", section 1): with logits Z = H W^T, lse_i = logsumexp(Z_i) and
+The operation (page "Een gefuseerde forward-kernel
+voor lineaire cross-entropy op Apple-GPU's", section 1): with logits Z = H W^T, lse_i = logsumexp(Z_i) and
 loss_i = lse_i - Z[i, y_i], both fp32 per token.
 
 If the library has not been built, importing this package raises: there is

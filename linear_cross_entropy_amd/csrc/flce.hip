@@ -2,8 +2,8 @@
 //
 // Computes, for H (N x D), W (V x D) and int32 targets y,
 //     lse_i  = logsumexp_v (H W^T)[i, v],     loss_i = lse_i - (H W^T)[i, y_i]
-// as defined on the page "A fused forward kernel for linear cross-entropy on
-// Apple GPUs" (section 1), without ever storing the N x V logits.
+// as defined on the page "Een gefuseerde forward-kernel
+// voor lineaire cross-entropy op Apple-GPU's" (section 1), without ever storing the N x V logits.
 //
 // Two launches on the caller's stream:
 //   1. flce_partials_kernel: a persistent-per-CU grid over (row block, vocab

@@ -2,8 +2,8 @@
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this package. It is a plain float64 CPU
-implementation of the definition on the page "A fused forward kernel for
-linear cross-entropy on Apple GPUs" (section 1): Z = H W^T and
+implementation of the definition on the page "Een gefuseerde forward-kernel
+voor lineaire cross-entropy op Apple-GPU's" (section 1): Z = H W^T and
 loss_i = logsumexp(Z_i) - Z_{i, y_i}. The arithmetic lives in
 ``flce_oracle.c`` (plain C, OpenMP over rows); this module only builds it and
 marshals arguments. It shares no code with the GPU library.

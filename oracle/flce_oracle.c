@@ -3,8 +3,8 @@
  * the tests, the smoke check and the benchmark's CPU-baseline leg use it to
  * judge the GPU library; the library never calls it.
  *
- * It is the plain definition from "A fused forward kernel for linear
- * cross-entropy on Apple GPUs" (section 1, the definition of plain
+ * It is the plain definition from "Een gefuseerde forward-kernel
+ * voor lineaire cross-entropy op Apple-GPU's" (section 1, the definition of plain
  * cross-entropy): with H an (N, D) matrix of hidden states and W a (V, D)
  * output projection, the logits are Z = H W^T and, for the target y_i,
  *     loss_i = logsumexp(Z_i) - Z_{i, y_i}.

@@ -3,8 +3,8 @@
 Each pin takes ``fwd(H, W, y, rows=None) -> (loss, lse, z_target)`` (float64
 numpy arrays) and raises AssertionError when the implementation disagrees with
 a closed form, an invariant, an exact brute force, or a hand-worked example.
-The definition pinned is the one on the page "A fused forward kernel for
-linear cross-entropy on Apple GPUs" (section 1): Z = H W^T,
+The definition pinned is the one on the page "Een gefuseerde forward-kernel
+voor lineaire cross-entropy op Apple-GPU's" (section 1): Z = H W^T,
 loss_i = logsumexp(Z_i) - Z_{i, y_i}.
 
 The same pins run against deliberately broken copies of the oracle in

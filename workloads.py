@@ -6,8 +6,8 @@ the CPU oracle, the tests and the benchmark can all use it without sharing any
 computation with the HIP path.
 
 The five named workloads restate the shapes and value distributions the
-benchmark contract quotes: the page "A fused forward kernel for linear
-cross-entropy on Apple GPUs" (section 3) measures one production shape,
+benchmark contract quotes: the page "Een gefuseerde forward-kernel
+voor lineaire cross-entropy op Apple-GPU's" (section 3) measures one production shape,
 N=8192, V=151936, D=4096 with bfloat16 inputs, and the others are smaller,
 odd-V and larger-vocabulary variants of it. No public dataset is involved.
 
