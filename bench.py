@@ -115,8 +115,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the forward shards by rows with no "
-              "communication, and multi-GPU runs are not part of this build. Use --gpus 1.",
+        print("bench.py measures one GPU only (the forward shards by rows with no "
+              "communication, so N GPUs run N independent copies). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

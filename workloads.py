@@ -5,13 +5,13 @@ This module only draws inputs: hidden states H (N x D), an output projection W
 the CPU oracle, the tests and the benchmark can all use it without sharing any
 computation with the HIP path.
 
-The five named workloads restate the shapes and value distributions the
-benchmark contract quotes: the page "Een gefuseerde forward-kernel
-voor lineaire cross-entropy op Apple-GPU's" (section 3) measures one production shape,
-N=8192, V=151936, D=4096 with bfloat16 inputs, and the others are smaller,
-odd-V and larger-vocabulary variants of it. No public dataset is involved.
+The five named workloads are the production case the page "Een gefuseerde
+forward-kernel voor lineaire cross-entropy op Apple-GPU's" measures (abstract and section 3:
+N=8192, V=151936, D=4096, bfloat16 inputs) and smaller, odd-V and
+larger-vocabulary variants of it, with the value distributions stated below.
+No public dataset is involved.
 
-Recipe (the readings are listed in the design doc):
+Recipe:
   * Values are drawn in fp32 from a torch.Generator on the device the tensors
     live on, seeded with 1000*config_index + stream (H=0, W=1, targets=2,
     outlier rows=3), then rounded once to the input dtype with
