@@ -1,10 +1,11 @@
-"""Oracle for the fused linear cross-entropy forward -- TEST INFRASTRUCTURE.
+"""Oracle for the fused linear cross-entropy forward and backward -- TEST INFRASTRUCTURE.
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 ``cpu_baseline`` leg may import this package. It is a plain float64 CPU
 implementation of the definition on the page "Een gefuseerde forward-kernel
 voor lineaire cross-entropy op Apple-GPU's" (section 1): Z = H W^T and
-loss_i = logsumexp(Z_i) - Z_{i, y_i}. The arithmetic lives in
+loss_i = logsumexp(Z_i) - Z_{i, y_i}, and the gradient of sum_i g_i loss_i
+with respect to H and W (the chain rule on that definition). The arithmetic lives in
 ``flce_oracle.c`` (plain C, OpenMP over rows); this module only builds it and
 marshals arguments. It shares no code with the GPU library.
 
@@ -50,6 +51,13 @@ def load(path: str | None = None):
         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+    ]
+    lib.oracle_lce_backward.restype = ctypes.c_int
+    lib.oracle_lce_backward.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
     ]
     lib.oracle_num_threads.restype = ctypes.c_int
     if path is None:
@@ -124,3 +132,55 @@ def forward(H, W, y, rows=None, lib=None):
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return loss, lse, zt
+
+
+def backward(H, W, y, g, rows=None, want_dW=True, lib=None):
+    """Gradient of sum_i g_i loss_i: returns a dict of float64 arrays
+    dH (R, D) and dH_abs for the selected rows (all rows if rows is None), and,
+    when want_dW, dW (V, D) and dW_abs over all rows. The *_abs arrays are the
+    sums of absolute values of each output's terms.
+
+    g: the upstream gradient per token (float32 or float64, length N); it is
+    widened exactly to float64.
+    """
+    lib = lib or load()
+    h, dt_h = _as_numpy(H)
+    w, dt_w = _as_numpy(W)
+    t, _ = _as_numpy(y)
+    if dt_h != dt_w or dt_h is None:
+        raise TypeError("H and W must share a floating dtype")
+    if t.dtype != np.int32:
+        raise TypeError("targets must be int32")
+    try:
+        import torch
+        if isinstance(g, torch.Tensor):
+            g = g.detach().cpu().numpy()
+    except ImportError:
+        pass
+    gd = np.ascontiguousarray(np.asarray(g, dtype=np.float64))
+    N, D = h.shape
+    V, D2 = w.shape
+    if D2 != D or t.shape != (N,) or gd.shape != (N,):
+        raise ValueError("shape mismatch")
+    if rows is None:
+        R, rows_arr = N, None
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        R = rows_arr.shape[0]
+    dH = np.empty((R, D), np.float64)
+    dH_abs = np.empty((R, D), np.float64)
+    dW = np.empty((V, D), np.float64) if want_dW else None
+    dW_abs = np.empty((V, D), np.float64) if want_dW else None
+    rc = lib.oracle_lce_backward(
+        h.ctypes.data, w.ctypes.data, t.ctypes.data, gd.ctypes.data, N, D, V, dt_h,
+        rows_arr.ctypes.data if rows_arr is not None else None, R,
+        dH.ctypes.data, dH_abs.ctypes.data,
+        dW.ctypes.data if want_dW else None, dW_abs.ctypes.data if want_dW else None)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    out = {"dH": dH, "dH_abs": dH_abs}
+    if want_dW:
+        out["dW"] = dW
+        out["dW_abs"] = dW_abs
+    return out
+

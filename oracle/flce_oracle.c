@@ -1,7 +1,8 @@
 /*
- * Oracle for the linear cross-entropy forward. TEST INFRASTRUCTURE ONLY:
- * the tests, the smoke check and the benchmark's CPU-baseline leg use it to
- * judge the GPU library; the library never calls it.
+ * Oracle for the linear cross-entropy forward and its backward.
+ * TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+ * CPU-baseline leg use it to judge the GPU library; the library never calls
+ * it.
  *
  * It is the plain definition from "Een gefuseerde forward-kernel
  * voor lineaire cross-entropy op Apple-GPU's" (section 1, the definition of plain
@@ -58,6 +59,27 @@ int oracle_num_threads(void) {
 }
 
 /*
+ * The V logits of row i, Z_i = H_i W^T, into z[0..V), and logsumexp(Z_i)
+ * in two passes: the maximum, then the shifted sum.
+ */
+static double row_logits_lse(const void* H, const void* W, int64_t D, int64_t V, int dtype,
+                             int64_t i, double* z) {
+  for (int64_t v = 0; v < V; ++v) {
+    double acc = 0.0;
+    for (int64_t d = 0; d < D; ++d)
+      acc += widen(H, dtype, i * D + d) * widen(W, dtype, v * D + d);
+    z[v] = acc;
+  }
+  double M = z[0];
+  for (int64_t v = 1; v < V; ++v)
+    if (z[v] > M || isnan(z[v])) M = z[v];
+  double S = 0.0;
+  for (int64_t v = 0; v < V; ++v) S += exp(z[v] - M);
+  double l = M + log(S);
+  return l;
+}
+
+/*
  * rows: R row indices into [0, N) (NULL means rows 0..N-1 with R = N).
  * Writes loss[r], lse[r], z_target[r] for r in [0, R).
  * Returns 0, or -1 on an invalid argument or a failed allocation.
@@ -86,20 +108,7 @@ int oracle_lce_forward(const void* H, const void* W, const int32_t* y,
         failed = 1;
         continue;
       }
-      /* Z_i = H_i W^T, one logit per vocabulary row. */
-      for (int64_t v = 0; v < V; ++v) {
-        double acc = 0.0;
-        for (int64_t d = 0; d < D; ++d)
-          acc += widen(H, dtype, i * D + d) * widen(W, dtype, v * D + d);
-        z[v] = acc;
-      }
-      /* logsumexp(Z_i), two passes: the maximum, then the shifted sum. */
-      double M = z[0];
-      for (int64_t v = 1; v < V; ++v)
-        if (z[v] > M || isnan(z[v])) M = z[v];
-      double S = 0.0;
-      for (int64_t v = 0; v < V; ++v) S += exp(z[v] - M);
-      double l = M + log(S);
+      const double l = row_logits_lse(H, W, D, V, dtype, i, z);
       lse[r] = l;
       int64_t t = (int64_t)y[i];
       if (t >= 0 && t < V) {
@@ -112,5 +121,109 @@ int oracle_lce_forward(const void* H, const void* W, const int32_t* y,
     }
     free(z);
   }
+  return failed ? -1 : 0;
+}
+
+/*
+ * Backward of the same definition, for an upstream gradient g (one value per
+ * token): the gradient of sum_i g_i loss_i. The page's training path keeps
+ * the forward log-sum-exp and regenerates the logits for its backward
+ * (section 1); the derivative itself is the chain rule applied to the
+ * definition above:
+ *     p_iv   = exp(z_iv - lse_i)                  (softmax of row i)
+ *     dZ_iv  = g_i (p_iv - [v == y_i])
+ *     dH_i   = sum_v dZ_iv W_v                    (N x D)
+ *     dW_v   = sum_i dZ_iv H_i                    (V x D)
+ * Reading where the page is silent: a target outside [0, V) matches no v, so
+ * that row contributes g_i p_i (the gradient of its lse alone); a caller that
+ * ignores such rows passes g_i = 0.
+ *
+ * Everything is float64, row by row, with the row's logits materialised; lse
+ * is recomputed here (two passes, as in the forward) rather than taken from
+ * anywhere else. Alongside each output the sum of the absolute values of its
+ * terms is returned (dH_abs_id = sum_v |dZ_iv W_vd|, dW_abs_vd =
+ * sum_i |dZ_iv H_id|), from which an error bound for a lower-precision
+ * evaluation of the same sums follows.
+ *
+ * rows: R row indices for dH (NULL: all N rows, R = N). dW (and dW_abs) need
+ * every row and are computed only when dW is not NULL; that keeps the N x V
+ * matrix dZ in memory, so it is for small shapes.
+ */
+/* dZ_i = g_i (softmax(Z_i) - onehot(y_i)) into dz[0..V). */
+static void row_dz(const void* H, const void* W, const int32_t* y, const double* g,
+                   int64_t D, int64_t V, int dtype, int64_t i, double* dz) {
+  const double l = row_logits_lse(H, W, D, V, dtype, i, dz);
+  const int64_t t = (int64_t)y[i];
+  for (int64_t v = 0; v < V; ++v) dz[v] = g[i] * (exp(dz[v] - l) - (v == t ? 1.0 : 0.0));
+}
+
+int oracle_lce_backward(const void* H, const void* W, const int32_t* y, const double* g,
+                        int64_t N, int64_t D, int64_t V, int dtype,
+                        const int64_t* rows, int64_t R,
+                        double* dH, double* dH_abs, double* dW, double* dW_abs) {
+  if (N < 0 || D < 1 || V < 1 || R < 0 || (dtype != 0 && dtype != 1)) return -1;
+  if (!rows) R = N;
+  if (N > 0 && (!H || !W || !y || !g)) return -1;
+  if (R > 0 && !dH) return -1;
+  double* dz_all = NULL;
+  if (dW) {
+    dz_all = (double*)malloc((size_t)(N > 0 ? N : 1) * (size_t)V * sizeof(double));
+    if (!dz_all) return -1;
+  }
+  int failed = 0;
+  /* dZ for every row, when dW is wanted */
+  if (dW) {
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < N; ++i) row_dz(H, W, y, g, D, V, dtype, i, dz_all + i * V);
+  }
+  /* dH for the selected rows */
+#pragma omp parallel
+  {
+    double* z = dz_all ? NULL : (double*)malloc((size_t)V * sizeof(double));
+    if (!dz_all && !z) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < R; ++r) {
+      if (!dz_all && !z) continue;
+      const int64_t i = rows ? rows[r] : r;
+      if (i < 0 || i >= N) {
+#pragma omp atomic write
+        failed = 1;
+        continue;
+      }
+      const double* dz = dz_all ? dz_all + i * V : z;
+      if (!dz_all) row_dz(H, W, y, g, D, V, dtype, i, z);
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0, aabs = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+          const double term = dz[v] * widen(W, dtype, v * D + d);  /* dZ_iv W_vd */
+          acc += term;
+          aabs += fabs(term);
+        }
+        dH[r * D + d] = acc;
+        if (dH_abs) dH_abs[r * D + d] = aabs;
+      }
+    }
+    free(z);
+  }
+  /* dW, every vocabulary row, summing over tokens in order */
+  if (dW && !failed) {
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t v = 0; v < V; ++v) {
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0, aabs = 0.0;
+        for (int64_t i = 0; i < N; ++i) {
+          const double term = dz_all[i * V + v] * widen(H, dtype, i * D + d);  /* dZ_iv H_id */
+          acc += term;
+          aabs += fabs(term);
+        }
+        dW[v * D + d] = acc;
+        if (dW_abs) dW_abs[v * D + d] = aabs;
+      }
+    }
+  }
+  free(dz_all);
   return failed ? -1 : 0;
 }

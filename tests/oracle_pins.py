@@ -285,3 +285,160 @@ ALL_PINS = [
     pin_out_of_range_target,
     pin_nan_propagates,
 ]
+
+
+# ---------------------------------------------------------------- backward pins
+# Each takes (fwd, bwd) with bwd(H, W, y, g, rows=None, want_dW=True) -> dict of
+# float64 arrays dH, dH_abs (rows), dW, dW_abs (all rows). The backward is the
+# gradient of sum_i g_i loss_i for the section 1 definition; the forward it is
+# checked against is already pinned above.
+
+def _richardson(f, x0: np.ndarray, idx, h: float) -> float:
+    """d f / d x[idx] by central differences at steps h and h/2, combined to
+    cancel the h^2 term. The steps are powers of two, so x +- h is exact in fp32
+    for the |x| used here."""
+    def central(step):
+        xp = x0.copy()
+        xm = x0.copy()
+        xp[idx] += np.float32(step)
+        xm[idx] -= np.float32(step)
+        return (f(xp) - f(xm)) / (2.0 * step)
+    return (4.0 * central(h / 2) - central(h)) / 3.0
+
+
+def pin_bwd_finite_differences(fwd, bwd):
+    """dH and dW against Richardson-extrapolated central differences of
+    sum_i g_i loss_i, evaluated with the forward oracle (fp32 inputs)."""
+    rng = np.random.default_rng(40)
+    for case, (N, D, V) in enumerate([(3, 5, 7), (2, 3, 1), (4, 2, 11)]):
+        Hn = (rng.standard_normal((N, D)) * 0.7).astype(np.float32)
+        Wn = (rng.standard_normal((V, D)) * 0.7).astype(np.float32)
+        y = _y(rng.integers(0, V, N))
+        g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+
+        def F_of_H(h):
+            loss, _, _ = fwd(_f32(h), _f32(Wn), y)
+            return float(np.dot(g.astype(np.float64), loss))
+
+        def F_of_W(w):
+            loss, _, _ = fwd(_f32(Hn), _f32(w), y)
+            return float(np.dot(g.astype(np.float64), loss))
+
+        out = bwd(_f32(Hn), _f32(Wn), y, g)
+        fd_H = np.array([[_richardson(F_of_H, Hn, (i, d), 2.0 ** -6) for d in range(D)] for i in range(N)])
+        fd_W = np.array([[_richardson(F_of_W, Wn, (v, d), 2.0 ** -6) for d in range(D)] for v in range(V)])
+        _close(out["dH"], fd_H, 2e-6, f"dH vs finite differences case {case}")
+        _close(out["dW"], fd_W, 2e-6, f"dW vs finite differences case {case}")
+
+
+def pin_bwd_zero_weights(fwd, bwd):
+    """W = 0: every row's softmax is uniform, so dH = sum_v dZ_iv W_v = 0 and
+    dW_v = sum_i g_i (1/V - [v == y_i]) H_i."""
+    rng = np.random.default_rng(41)
+    N, D, V = 5, 6, 9
+    Hn = rng.standard_normal((N, D)).astype(np.float32)
+    yn = rng.integers(0, V, N)
+    g = rng.uniform(-1, 1, N).astype(np.float32)
+    out = bwd(_f32(Hn), _f32(np.zeros((V, D))), _y(yn), g)
+    _close(out["dH"], np.zeros((N, D)), 0.0, "W=0 dH")
+    want = np.zeros((V, D))
+    for i in range(N):
+        for v in range(V):
+            want[v] += float(g[i]) * ((1.0 / V) - (1.0 if v == yn[i] else 0.0)) * Hn[i].astype(np.float64)
+    _close(out["dW"], want, 1e-14, "W=0 dW")
+
+
+def pin_bwd_single_word(fwd, bwd):
+    """V = 1: softmax is 1 and so is the one-hot, so both gradients vanish."""
+    rng = np.random.default_rng(42)
+    H = _bf16(rng.standard_normal((3, 8)))
+    W = _bf16(rng.standard_normal((1, 8)))
+    out = bwd(H, W, _y([0, 0, 0]), np.ones(3, np.float32))
+    _close(out["dH"], np.zeros((3, 8)), 0.0, "V=1 dH")
+    _close(out["dW"], np.zeros((1, 8)), 0.0, "V=1 dW")
+
+
+def pin_bwd_identities(fwd, bwd):
+    """sum_v dZ_iv = 0 for a valid target, so sum_v dW_v = 0; and
+    <dH, H> = <dW, W> = sum_iv dZ_iv z_iv; each output is bounded by the sum
+    of the absolute values of its terms."""
+    rng = np.random.default_rng(43)
+    N, D, V = 6, 16, 50
+    H = _bf16(rng.standard_normal((N, D)))
+    W = _bf16(rng.standard_normal((V, D)) * 0.5)
+    y = _y(rng.integers(0, V, N))
+    g = rng.uniform(0.1, 2.0, N).astype(np.float32)
+    out = bwd(H, W, y, g)
+    colsum = out["dW"].sum(axis=0)
+    scale = out["dW_abs"].sum(axis=0)
+    assert np.all(np.abs(colsum) <= 1e-12 * scale), "sum over the vocabulary of dW is not 0"
+    lhs = float((out["dH"] * H.double().numpy()).sum())
+    rhs = float((out["dW"] * W.double().numpy()).sum())
+    assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs)), f"<dH,H>={lhs} != <dW,W>={rhs}"
+    assert np.all(out["dH_abs"] >= np.abs(out["dH"])) and np.all(out["dW_abs"] >= np.abs(out["dW"]))
+
+
+def pin_bwd_out_of_range_target(fwd, bwd):
+    """A target outside [0, V) matches no vocabulary entry: that row's dH is
+    g_i times the gradient of its lse (checked by finite differences of the
+    forward's lse); other rows are unchanged."""
+    rng = np.random.default_rng(44)
+    N, D, V = 3, 4, 6
+    Hn = (rng.standard_normal((N, D)) * 0.5).astype(np.float32)
+    Wn = (rng.standard_normal((V, D)) * 0.5).astype(np.float32)
+    g = np.array([0.75, 1.25, 0.5], np.float32)
+    good = _y([1, 4, 2])
+    bad = _y([-1, 4, 2])
+    ob = bwd(_f32(Hn), _f32(Wn), bad, g)
+    og = bwd(_f32(Hn), _f32(Wn), good, g)
+    _close(ob["dH"][1:], og["dH"][1:], 0.0, "rows next to the bad target")
+
+    def lse0(h):
+        _, lse, _ = fwd(_f32(h), _f32(Wn), bad)
+        return float(g[0]) * float(lse[0])
+
+    fd = np.array([_richardson(lse0, Hn, (0, d), 2.0 ** -6) for d in range(D)])
+    _close(ob["dH"][0], fd, 2e-6, "out-of-range row = g * d lse / d H")
+
+
+def pin_bwd_rows_subset(fwd, bwd):
+    """dH for a subset of rows, in any order, equals those rows of the full run."""
+    rng = np.random.default_rng(45)
+    N, D, V = 7, 8, 40
+    H = _bf16(rng.standard_normal((N, D)))
+    W = _bf16(rng.standard_normal((V, D)))
+    y = _y(rng.integers(0, V, N))
+    g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    full = bwd(H, W, y, g)
+    sub = bwd(H, W, y, g, rows=[5, 0, 3], want_dW=False)
+    _close(sub["dH"], full["dH"][[5, 0, 3]], 0.0, "row subset dH")
+
+
+def pin_bwd_autograd(fwd, bwd):
+    """Agreement with float64 reverse-mode differentiation of the definition in
+    torch (an independent implementation of the same derivative)."""
+    rng = np.random.default_rng(46)
+    N, D, V = 6, 12, 37
+    H = _bf16(rng.standard_normal((N, D)))
+    W = _bf16(rng.standard_normal((V, D)))
+    y = _y(rng.integers(0, V, N))
+    g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    out = bwd(H, W, y, g)
+    Hd = H.double().clone().requires_grad_()
+    Wd = W.double().clone().requires_grad_()
+    Z = Hd @ Wd.T
+    loss = torch.logsumexp(Z, dim=1) - Z.gather(1, y.long()[:, None])[:, 0]
+    (loss * torch.as_tensor(g, dtype=torch.float64)).sum().backward()
+    _close(out["dH"], Hd.grad.numpy(), 1e-13, "dH vs autograd")
+    _close(out["dW"], Wd.grad.numpy(), 1e-13, "dW vs autograd")
+
+
+BWD_PINS = [
+    pin_bwd_finite_differences,
+    pin_bwd_zero_weights,
+    pin_bwd_single_word,
+    pin_bwd_identities,
+    pin_bwd_out_of_range_target,
+    pin_bwd_rows_subset,
+    pin_bwd_autograd,
+]

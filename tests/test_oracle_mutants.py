@@ -1,4 +1,5 @@
-"""Plant plausible mistakes in copies of the oracle and check the pins catch each.
+"""Plant plausible mistakes in copies of the oracle (forward and backward) and
+check the pins catch each.
 
 Every mutant is a textual edit of oracle/flce_oracle.c compiled to a private
 library on the CPU; the real oracle is never modified. A mutant that passes
@@ -10,7 +11,7 @@ import tempfile
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS
+from oracle_pins import ALL_PINS, BWD_PINS
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "flce_oracle.c")
 
@@ -22,16 +23,29 @@ MUTANTS = {
     "lse_sign": ("double l = M + log(S);", "double l = M - log(S);"),
     "log_base2": ("double l = M + log(S);", "double l = M + log2(S);"),
     "loss_sign": ("loss[r] = l - z[t];", "loss[r] = z[t] - l;"),
-    "no_max_shift": ("S += exp(z[v] - M);\n      double l = M + log(S);",
-                     "S += exp(z[v]);\n      double l = log(S);"),
+    "no_max_shift": ("S += exp(z[v] - M);\n  double l = M + log(S);",
+                     "S += exp(z[v]);\n  double l = log(S);"),
     "zero_init_max": ("double M = z[0];", "double M = 0.0;"),
-    "transposed_W": ("widen(W, dtype, v * D + d)", "widen(W, dtype, d * V + v)"),
-    "transposed_H": ("widen(H, dtype, i * D + d)", "widen(H, dtype, d * N + i)"),
-    "drop_first_feature": ("for (int64_t d = 0; d < D; ++d)", "for (int64_t d = 1; d < D; ++d)"),
+    "transposed_W": ("acc += widen(H, dtype, i * D + d) * widen(W, dtype, v * D + d);",
+                     "acc += widen(H, dtype, i * D + d) * widen(W, dtype, d * V + v);"),
+    "reversed_features_H": ("acc += widen(H, dtype, i * D + d) * widen(W, dtype, v * D + d);",
+                            "acc += widen(H, dtype, i * D + (D - 1 - d)) * widen(W, dtype, v * D + d);"),
+    "drop_first_feature": ("for (int64_t d = 0; d < D; ++d)\n      acc += widen(H",
+                           "for (int64_t d = 1; d < D; ++d)\n      acc += widen(H"),
     "neighbour_target": ("loss[r] = l - z[t];", "loss[r] = l - z[(t + 1) % V];"),
     "lse_minus_target_twice": ("lse[r] = l;", "lse[r] = l - z[0];"),
     "bf16_high_half_wrong": ("(uint32_t)((const uint16_t*)base)[idx] << 16",
                              "(uint32_t)((const uint16_t*)base)[idx] << 15"),
+    # backward
+    "bwd_onehot_sign": ("(exp(dz[v] - l) - (v == t ? 1.0 : 0.0))", "(exp(dz[v] - l) + (v == t ? 1.0 : 0.0))"),
+    "bwd_no_upstream": ("dz[v] = g[i] * (exp(", "dz[v] = (exp("),
+    "bwd_neighbour_target": ("(v == t ? 1.0 : 0.0)", "(v == (t + 1) % V ? 1.0 : 0.0)"),
+    "bwd_unnormalised_softmax": ("(exp(dz[v] - l) -", "(exp(dz[v]) -"),
+    "bwd_dH_transposed_W": ("dz[v] * widen(W, dtype, v * D + d);", "dz[v] * widen(W, dtype, d * V + v);"),
+    "bwd_dW_reversed_rows": ("dz_all[i * V + v] * widen(H, dtype, i * D + d);",
+                             "dz_all[i * V + v] * widen(H, dtype, (N - 1 - i) * D + d);"),
+    "bwd_dW_drop_last_row": ("for (int64_t i = 0; i < N; ++i) {\n          const double term = dz_all",
+                             "for (int64_t i = 0; i < N - 1; ++i) {\n          const double term = dz_all"),
 }
 
 
@@ -50,10 +64,18 @@ def test_pins_catch_mutant(name):
         def fwd(H, W, y, rows=None):
             return oracle.forward(H, W, y, rows=rows, lib=lib)
 
+        def bwd(H, W, y, g, rows=None, want_dW=True):
+            return oracle.backward(H, W, y, g, rows=rows, want_dW=want_dW, lib=lib)
+
         caught = []
         for pin in ALL_PINS:
             try:
                 pin(fwd)
+            except (AssertionError, ValueError, FloatingPointError):
+                caught.append(pin.__name__)
+        for pin in BWD_PINS:
+            try:
+                pin(fwd, bwd)
             except (AssertionError, ValueError, FloatingPointError):
                 caught.append(pin.__name__)
         assert caught, f"no pin catches mutant {name}"
