@@ -1,5 +1,6 @@
 /*
- * flce.h -- fused linear cross-entropy forward on AMD Instinct MI355X (gfx950).
+ * flce.h -- fused linear cross-entropy forward and backward on AMD Instinct
+ * MI355X (gfx950).
  *
  * The operation is the one defined on the page "Een gefuseerde forward-kernel
  * voor lineaire cross-entropy op Apple-GPU's" (section 1): for hidden states H
@@ -17,8 +18,8 @@
  * block) is at most a few hundred.
  *
  * Conventions for every entry point:
- *   - H, W, targets, loss_out, lse_out and workspace are DEVICE pointers owned
- *     by the caller. The library never frees them and keeps none of them
+ *   - H, W, targets, loss_out, lse_out, workspace (and, for the backward,
+ *     lse, grad_loss, dH and dW) are DEVICE pointers owned by the caller. The library never frees them and keeps none of them
  *     after the call returns.
  *   - H is N x D and W is V x D, row-major and dense (row stride D elements),
  *     both of `dtype`. They must be 16-byte aligned and D * sizeof(element)
@@ -116,6 +117,44 @@ int flce_partials(const void* H, const void* W, const int32_t* targets,
 int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtype,
                float* loss_out, float* lse_out,
                const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of the same loss, for an upstream gradient g = grad_loss (one
+ * float32 per token; g_i = 1/N for a mean over tokens): the gradients of
+ * sum_i g_i loss_i,
+ *
+ *     dZ_iv = g_i (softmax(Z_i)_v - [v == y_i]),   dH = dZ W,   dW = dZ^T H,
+ *
+ * by the chain rule on the section 1 definition. As on the page (section 1:
+ * the training path keeps the forward's log-sum-exp and regenerates the
+ * logits tile by tile for its backward), `lse` is the forward's lse_out for
+ * the same H, W and targets, and Z is recomputed, never stored whole.
+ *
+ *   - dH (N x D) and dW (V x D) are float32 DEVICE outputs, row-major, fully
+ *     overwritten (N == 0 writes dW = 0 and reads nothing else).
+ *   - A target outside [0, V) matches no vocabulary row: that row contributes
+ *     g_i softmax(Z_i), the gradient of its lse alone. Pass g_i = 0 to leave a
+ *     row out.
+ *   - dZ is rounded to `dtype` before the two products (fp32 accumulation);
+ *     the result differs from exact arithmetic by about the unit roundoff of
+ *     `dtype` times the sum of the absolute values of each output's terms.
+ *   - Rows are processed in chunks of R rows; the workspace
+ *     (flce_backward_workspace_bytes, 256-byte aligned, FLCE_ERR_INVALID_ARG
+ *     if smaller) holds W transposed (D x V), one chunk of H transposed and
+ *     dZ of one chunk in both orientations, about 4 GiB at most for dZ.
+ *     Allocates nothing.
+ *   - Other conventions (alignment, D * sizeof(element) % 16 == 0, stream,
+ *     status codes) as for the forward.
+ */
+int flce_backward(const void* H, const void* W, const int32_t* targets,
+                  const float* lse, const float* grad_loss,
+                  int64_t N, int64_t D, int64_t V, int dtype,
+                  float* dH, float* dW,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes flce_backward needs for a shape (0 for an invalid or
+ * unsupported shape). */
+size_t flce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
 
 /* Tile plan for a shape; FLCE_ERR_INVALID_ARG/UNSUPPORTED as flce_forward. */
 int flce_get_plan(int64_t N, int64_t D, int64_t V, int dtype, flce_plan_t* plan);

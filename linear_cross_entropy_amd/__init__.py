@@ -1,5 +1,5 @@
-"""Python binding of libflce.so, the fused linear cross-entropy forward for
-AMD Instinct MI355X (gfx950).
+"""Python binding of libflce.so, the fused linear cross-entropy forward (and
+its backward) for AMD Instinct MI355X (gfx950).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI declared in ``include/flce.h``. PyTorch supplies the
@@ -11,6 +11,8 @@ device memory and the stream. The functions keep the C names:
     flce_merge(targets, D, V, dtype, workspace, loss=None, lse=None, stream=None)
     flce_workspace_bytes(N, D, V, dtype) -> int
     flce_get_plan(N, D, V, dtype) -> dict
+    flce_backward(H, W, targets, lse, grad_loss, workspace=None, dH=None, dW=None, stream=None)
+    flce_backward_workspace_bytes(N, D, V, dtype) -> int
     flce_status_string(status) -> str
     flce_version() -> int
 
@@ -58,6 +60,10 @@ _lib.flce_merge.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp
 _lib.flce_merge.restype = _i32
 _lib.flce_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 _lib.flce_workspace_bytes.restype = _sz
+_lib.flce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.flce_backward.restype = _i32
+_lib.flce_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
+_lib.flce_backward_workspace_bytes.restype = _sz
 _lib.flce_status_string.argtypes = [_i32]
 _lib.flce_status_string.restype = ctypes.c_char_p
 _lib.flce_version.argtypes = []
@@ -79,7 +85,8 @@ _lib.flce_get_plan.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(FlcePlan)]
 _lib.flce_get_plan.restype = _i32
 
 EXPORTED = ["flce_forward", "flce_forward_ws", "flce_partials", "flce_merge",
-            "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version"]
+            "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version",
+            "flce_backward", "flce_backward_workspace_bytes"]
 
 
 class FlceError(RuntimeError):
@@ -214,6 +221,48 @@ def flce_merge(targets, D: int, V: int, dtype, ws, loss=None, lse=None, stream=N
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_merge")
     return loss, lse
+
+
+def flce_backward_workspace_bytes(N: int, D: int, V: int, dtype) -> int:
+    return int(_lib.flce_backward_workspace_bytes(N, D, V, _dtype_arg(dtype)))
+
+
+def _vec(t, N, device, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.shape != (N,) \
+            or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 ({N},) tensor on {device}")
+    return t
+
+
+def _mat(t, rows, cols, device, name):
+    if t is None:
+        return torch.empty(rows, cols, dtype=torch.float32, device=device)
+    if t.dtype != torch.float32 or t.shape != (rows, cols) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 ({rows}, {cols}) tensor on {device}")
+    return t
+
+
+def flce_backward(H, W, targets, lse, grad_loss, workspace=None, dH=None, dW=None, stream=None):
+    """(dH, dW) = gradients of sum_i grad_loss[i] * loss_i, float32; lse is the
+    forward's lse for the same inputs. The workspace (flce_backward_workspace_bytes)
+    is allocated here when not given."""
+    N, D, V, dt = _check_inputs(H, W, targets)
+    dev = H.device
+    lse = _vec(lse, N, dev, "lse")
+    grad_loss = _vec(grad_loss, N, dev, "grad_loss")
+    dH = _mat(dH, N, D, dev, "dH")
+    dW = _mat(dW, V, D, dev, "dW")
+    nbytes = flce_backward_workspace_bytes(N, D, V, dt)
+    if nbytes == 0:
+        raise FlceError(FLCE_ERR_UNSUPPORTED, "flce_backward_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rc = _lib.flce_backward(_ptr(H), _ptr(W), _ptr(targets), _ptr(lse), _ptr(grad_loss), N, D, V, dt,
+                            _ptr(dH), _ptr(dW), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream_ptr(stream, dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_backward")
+    return dH, dW
 
 
 def forward(H, W, targets):

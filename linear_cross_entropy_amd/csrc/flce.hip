@@ -25,8 +25,11 @@
 // different grouping of the vocabulary.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include "flce.h"
 
@@ -89,16 +92,37 @@ typedef TileCfg<256, 256, 2, 4> Tile256;
 typedef TileCfg<320, 256, 2, 4> Tile320;
 typedef TileCfg<384, 256, 2, 4> Tile384;
 
-struct PartialsArgs {
-  const char* H;
-  const char* W;
-  const int32_t* y;
+// What the tile loop does with each finished tile of Z = A B^T (A: the rows
+// along the tile's vocabulary axis, B: the rows along its token axis).
+enum TileMode {
+  kForward = 0,  // online (max, sum) per token, target capture, per-chunk partials
+  kDz = 1,       // dZ = g (softmax - onehot), written row-major and transposed
+  kGemm = 2,     // plain C[a][b] = Z (or C += Z)
+};
+
+struct TileArgs {
+  const char* H;      // B operand: b_rows x K (tokens in the forward)
+  const char* W;      // A operand: a_rows x K (vocabulary rows in the forward)
+  int N, V, row_bytes;  // b_rows, a_rows, K in bytes (both operands' row length)
+  int row_blocks, vocab_tiles, chunks;
+  int xcd_rows, xcd_chunks;  // XCD group shape; xcd_rows == 0 disables the remap
+  // kForward and kDz
+  const int32_t* y;   // [N] targets
+  // kForward
   float* part_m;      // [chunks][N]
   float* part_s;      // [chunks][N]
   float* z_target;    // [N]
-  int N, V, row_bytes;
-  int row_blocks, vocab_tiles, chunks;
-  int xcd_rows, xcd_chunks;  // XCD group shape; xcd_rows == 0 disables the remap
+  // kDz: lse and upstream gradient per token; dZ as [tok][dz_ld] and [v][dzt_ld]
+  const float* lse;
+  const float* grad;
+  char* dz;
+  char* dzt;
+  int dz_ld, dzt_ld;  // row lengths in elements (>= the valid extents; the rest is written as 0)
+  int dz_rows;        // tokens to write in dz / columns in dzt (N rounded up)
+  int dz_cols;        // vocabulary rows to write (V rounded up)
+  // kGemm
+  float* C;           // [V][ldc] fp32
+  int ldc, accumulate;
 };
 
 // Element-type specific pieces: a 16-byte fragment and the matrix-core step
@@ -155,8 +179,23 @@ __device__ __forceinline__ void combine(float& m, float& s, float m2, float s2) 
   m = M;
 }
 
-template <typename T, typename C>
-__global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsArgs p) {
+// Four consecutive elements to (8- or 16-byte aligned) global memory.
+__device__ __forceinline__ void store4(char* dst, const __bf16 (&q)[4]) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  const bf16x4 v = {q[0], q[1], q[2], q[3]};
+  *(bf16x4*)dst = v;
+}
+__device__ __forceinline__ void store4(char* dst, const float (&q)[4]) {
+  const f32x4 v = {q[0], q[1], q[2], q[3]};
+  *(f32x4*)dst = v;
+}
+
+// The tile loop shared by the forward, the backward's dZ pass and the
+// backward's products: one workgroup owns a block of kBT B rows and a chunk of
+// kBV-row A tiles, contracts each tile over the whole of K on the matrix cores
+// and hands the finished tile, in registers, to the MODE's epilogue.
+template <typename T, typename C, int MODE>
+__device__ __forceinline__ void tile_loop(const TileArgs& p) {
   typedef typename Mma<T>::frag Frag;
   constexpr int kBV = C::BV, kBT = C::BT, kWavesV = C::WAVES_V;
   constexpr int WV = C::WV, WT = C::WT, MB = C::MB, NB = C::NB;
@@ -287,6 +326,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
   float m_run[NB], s_run[NB], zt[NB];
   bool zhit[NB];
   int ytok[NB];
+  float l2tok[NB], gtok[NB];  // kDz: lse * log2(e) and the upstream gradient of each token
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m_run[nb] = kNegInf;
@@ -294,7 +334,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
     zt[nb] = 0.f;
     zhit[nb] = false;
     const int tok = t0 + wt * WT + nb * 32 + (lane & 31);
-    ytok[nb] = tok < p.N ? p.y[tok] : -1;
+    ytok[nb] = -1;
+    l2tok[nb] = 0.f;
+    gtok[nb] = 0.f;
+    if constexpr (MODE != kGemm) {
+      if (tok < p.N) ytok[nb] = p.y[tok];
+    }
+    if constexpr (MODE == kDz) {
+      if (tok < p.N) {
+        l2tok[nb] = p.lse[tok] * kLog2e;
+        gtok[nb] = p.grad[tok];
+      }
+    }
   }
 
   f32x16 acc[MB][NB];
@@ -364,59 +415,112 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
     if (++ks < KS) continue;
     ks = 0;
 
-    // ---- epilogue of one vocabulary tile, entirely in registers
-    const int vw = (tile_begin + tile) * kBV + a_row;   // first vocabulary row of this wave
+    const int vw = (tile_begin + tile) * kBV + a_row;   // first A row (vocabulary row) of this wave
     ++tile;
-    if (vw + WV > p.V) {
-      // ragged last tile: vocabulary rows >= V are not logits at all
-      int lim = p.V - vw - 4 * (lane >> 5);
-      asm volatile("" : "+v"(lim));  // compared here, not hoisted as per-register lane masks
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (mb * 32 + 8 * (r >> 2) + (r & 3) >= lim) acc[mb][nb][r] = kNegInf;
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      // target logit: kept by the one lane holding (y, token); written at the end of the chunk
-      const int rel = ytok[nb] - vw;
-      if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & 1) == (lane >> 5)) {
-        int want = rel;
-        asm volatile("" : "+v"(want));  // likewise
-        const int want_mb = want >> 5;
-        const int want_r = ((want & 31) >> 3) * 4 + (want & 3);
-        float val = 0.f;
+    if constexpr (MODE == kForward) {
+      // ---- epilogue of one vocabulary tile, entirely in registers
+      if (vw + WV > p.V) {
+        // ragged last tile: vocabulary rows >= V are not logits at all
+        int lim = p.V - vw - 4 * (lane >> 5);
+        asm volatile("" : "+v"(lim));  // compared here, not hoisted as per-register lane masks
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (mb == want_mb && r == want_r) val = acc[mb][nb][r];
-        zt[nb] = val;
-        zhit[nb] = true;
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (mb * 32 + 8 * (r >> 2) + (r & 3) >= lim) acc[mb][nb][r] = kNegInf;
       }
-      // online update: m' = max(m, m_tile), s' = s e^(m - m') + sum_j e^(z_j - m')
-      float tmax = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+      for (int nb = 0; nb < NB; ++nb) {
+        // target logit: kept by the one lane holding (y, token); written at the end of the chunk
+        const int rel = ytok[nb] - vw;
+        if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & 1) == (lane >> 5)) {
+          int want = rel;
+          asm volatile("" : "+v"(want));  // likewise
+          const int want_mb = want >> 5;
+          const int want_r = ((want & 31) >> 3) * 4 + (want & 3);
+          float val = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
-      const float m_new = fmaxf(m_run[nb], tmax);
-      const float c = (m_new == kNegInf) ? 0.f : off2(m_new);
-      float s0 = 0.f, s1 = 0.f;
+          for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], kLog2e, -c));
-          s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r + 1], kLog2e, -c));
+            for (int r = 0; r < 16; ++r)
+              if (mb == want_mb && r == want_r) val = acc[mb][nb][r];
+          zt[nb] = val;
+          zhit[nb] = true;
         }
-      s_run[nb] = s_run[nb] * __builtin_amdgcn_exp2f(off2(m_run[nb]) - c) + (s0 + s1);
-      m_run[nb] = m_new;
+        // online update: m' = max(m, m_tile), s' = s e^(m - m') + sum_j e^(z_j - m')
+        float tmax = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
+        const float m_new = fmaxf(m_run[nb], tmax);
+        const float c = (m_new == kNegInf) ? 0.f : off2(m_new);
+        float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], kLog2e, -c));
+            s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r + 1], kLog2e, -c));
+          }
+        s_run[nb] = s_run[nb] * __builtin_amdgcn_exp2f(off2(m_run[nb]) - c) + (s0 + s1);
+        m_run[nb] = m_new;
+      }
+    } else if constexpr (MODE == kDz) {
+      // ---- dZ = g (softmax(Z) - onehot(y)) of one tile, with
+      // softmax = 2^(z log2(e) - lse log2(e)); rows >= V and tokens >= N are 0.
+      // Written to dz[tok][v] (four consecutive v per lane and register group)
+      // and dzt[v][tok] (32 consecutive tokens per half-wave).
+      const int v_lane = vw + 4 * (lane >> 5);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int tok = t0 + wt * WT + nb * 32 + (lane & 31);
+        if (tok >= p.dz_rows) continue;
+        const bool tok_ok = tok < p.N;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int v0 = v_lane + mb * 32 + 8 * r4;   // rows v0 .. v0 + 3 in registers 4*r4 ..
+            if (v0 >= p.dz_cols) continue;
+            T q[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int v = v0 + j;
+              float d = 0.f;
+              if (tok_ok && v < p.V) {
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][4 * r4 + j], kLog2e, -l2tok[nb]));
+                d = gtok[nb] * (v == ytok[nb] ? e - 1.f : e);
+              }
+              q[j] = (T)d;
+              *(T*)(p.dzt + ((size_t)v * p.dzt_ld + tok) * sizeof(T)) = q[j];
+            }
+            store4(p.dz + ((size_t)tok * p.dz_ld + v0) * sizeof(T), q);
+          }
+      }
+    } else {
+      // ---- C[a][b] = Z (or C += Z) for a < V, b < N
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = t0 + wt * WT + nb * 32 + (lane & 31);
+        if (b >= p.N) continue;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int a = vw + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (a < p.V) {
+              float* c = p.C + (size_t)a * p.ldc + b;
+              *c = p.accumulate ? *c + acc[mb][nb][r] : acc[mb][nb][r];
+            }
+          }
+      }
     }
   }
+
+  if constexpr (MODE != kForward) return;
 
   // ---- target logits found in this chunk
 #pragma unroll
@@ -459,6 +563,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(PartialsAr
   }
 }
 
+template <typename T, typename C>
+__global__ __launch_bounds__(C::THREADS, 1) void flce_partials_kernel(TileArgs p) {
+  tile_loop<T, C, kForward>(p);
+}
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::THREADS, 1) void flce_dz_kernel(TileArgs p) {
+  tile_loop<T, C, kDz>(p);
+}
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::THREADS, 1) void flce_gemm_kernel(TileArgs p) {
+  tile_loop<T, C, kGemm>(p);
+}
+
 // Merge: one thread per token, in double precision (a handful of operations
 // per row). With off(m) = fl(m log2 e) as in the partials kernel,
 // C = max_c off(m_c), S = sum_c s_c 2^(off(m_c) - C), lse = (C + log2 S) ln 2
@@ -483,6 +602,36 @@ __global__ __launch_bounds__(256) void flce_merge_kernel(const float* __restrict
   if (lse) lse[i] = (float)l;
   const int t = y[i];
   loss[i] = (t >= 0 && t < V) ? (float)(l - (double)z_target[i]) : __builtin_nanf("");
+}
+
+// ------------------------------------------------------------------ backward helpers
+// out[c][r] = in[r][c] for c < cols and r < rows, and 0 for rows <= r < out_len:
+// the backward's K-contiguous copies of W (vocabulary along K) and of a chunk
+// of H (tokens along K). 64 x 64 tiles staged through LDS; the extra column
+// keeps the transposed LDS reads on distinct banks.
+template <typename T>
+__global__ __launch_bounds__(256) void flce_transpose_kernel(const T* __restrict__ in, int rows, int cols,
+                                                             int64_t ld_in, T* __restrict__ out,
+                                                             int64_t ld_out, int out_len) {
+  __shared__ T tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll 4
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < rows && c < cols) ? in[(size_t)r * ld_in + c] : (T)0.f;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < cols && r < out_len) out[(size_t)c * ld_out + r] = tile[tx][i];
+  }
+}
+
+// dst[0..n) = 0.
+__global__ __launch_bounds__(256) void flce_zero_kernel(float* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
 }
 
 // ------------------------------------------------------------------ host side
@@ -632,15 +781,13 @@ int check_workspace(const Plan& pl, const void* ws, size_t bytes) {
   return FLCE_OK;
 }
 
-int launch_partials(const Plan& pl, const void* H, const void* W, const int32_t* y, void* ws,
-                    hipStream_t stream) {
-  PartialsArgs a;
-  a.H = (const char*)H;
-  a.W = (const char*)W;
-  a.y = y;
-  a.part_m = (float*)((char*)ws + pl.off_m);
-  a.part_s = (float*)((char*)ws + pl.off_s);
-  a.z_target = (float*)((char*)ws + pl.off_z);
+// Arguments of the tile loop for a plan: B rows (H role) x A rows (W role),
+// both row_bytes long.
+TileArgs tile_args(const Plan& pl, const void* B, const void* A) {
+  TileArgs a;
+  memset(&a, 0, sizeof a);
+  a.H = (const char*)B;
+  a.W = (const char*)A;
   a.N = pl.N;
   a.V = pl.V;
   a.row_bytes = pl.row_bytes;
@@ -649,14 +796,30 @@ int launch_partials(const Plan& pl, const void* H, const void* W, const int32_t*
   a.chunks = pl.chunks;
   a.xcd_rows = pl.xcd_rows;
   a.xcd_chunks = pl.xcd_chunks;
-  if (pl.dtype == FLCE_FP32)
-    hipLaunchKernelGGL((flce_partials_kernel<float, Tile256>), dim3(pl.grid), dim3(Tile256::THREADS), 0, stream, a);
-  else if (pl.tile == kTile384)
-    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile384>), dim3(pl.grid), dim3(Tile384::THREADS), 0, stream, a);
-  else if (pl.tile == kTile320)
-    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile320>), dim3(pl.grid), dim3(Tile320::THREADS), 0, stream, a);
-  else
-    hipLaunchKernelGGL((flce_partials_kernel<__bf16, Tile256>), dim3(pl.grid), dim3(Tile256::THREADS), 0, stream, a);
+  return a;
+}
+
+// Launch KERNEL<T, Tile> for the plan's dtype and tile (fp32 runs 256x256 only).
+#define FLCE_LAUNCH_TILES(KERNEL, pl, args, stream)                                                     \
+  do {                                                                                                  \
+    if ((pl).dtype == FLCE_FP32)                                                                        \
+      hipLaunchKernelGGL((KERNEL<float, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args);  \
+    else if ((pl).tile == kTile384)                                                                     \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile384>), dim3((pl).grid), dim3(Tile384::THREADS), 0, stream, args); \
+    else if ((pl).tile == kTile320)                                                                     \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile320>), dim3((pl).grid), dim3(Tile320::THREADS), 0, stream, args); \
+    else                                                                                                \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args); \
+  } while (0)
+
+int launch_partials(const Plan& pl, const void* H, const void* W, const int32_t* y, void* ws,
+                    hipStream_t stream) {
+  TileArgs a = tile_args(pl, H, W);
+  a.y = y;
+  a.part_m = (float*)((char*)ws + pl.off_m);
+  a.part_s = (float*)((char*)ws + pl.off_s);
+  a.z_target = (float*)((char*)ws + pl.off_z);
+  FLCE_LAUNCH_TILES(flce_partials_kernel, pl, a, stream);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -667,6 +830,132 @@ int launch_merge(const Plan& pl, const int32_t* y, float* loss, float* lse, cons
   const float* z = (const float*)((const char*)ws + pl.off_z);
   hipLaunchKernelGGL(flce_merge_kernel, dim3((pl.N + 255) / 256), dim3(256), 0, stream, m, s, z, y,
                      pl.N, pl.V, pl.chunks, loss, lse);
+  return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ backward
+// The backward runs over chunks of R rows. Per chunk: the dZ pass recomputes
+// Z for the chunk (the forward's tile loop, full D) and writes
+// dZ = g (softmax - onehot) in the input dtype twice, dz[R][Vp] and
+// dzt[Vp][Rp]; then dH[chunk] = dz . W (B operand: W transposed, [D][Vp]) and
+// dW (+)= dzt . H[chunk] (B operand: the chunk of H transposed, [D][Rp]), both
+// on the same tile loop with a store epilogue. Vp and Rp round V and R up to
+// 8 elements (16-byte rows); the padding is written as zeros.
+constexpr double kDzBudget = 4.0 * 1024 * 1024 * 1024;  // bytes for dz + dzt
+
+struct BwdPlan {
+  int64_t N, D, V, Vp, R, Rp;
+  int dtype, chunks;
+  size_t es, off_wt, off_ht, off_dz, off_dzt, ws_bytes;
+};
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
+  if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
+  if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
+  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
+  if ((D * es) % 16 != 0) return FLCE_ERR_UNSUPPORTED;
+  if (N > INT32_MAX / 2 || V > INT32_MAX / 2 || D > INT32_MAX / 2) return FLCE_ERR_UNSUPPORTED;
+  bp->N = N;
+  bp->D = D;
+  bp->V = V;
+  bp->dtype = dtype;
+  bp->es = (size_t)es;
+  bp->Vp = round_up(V, 8);
+  if (N > 0) {
+    const double per_row = 2.0 * (double)bp->Vp * (double)es;
+    int64_t nc = (int64_t)((double)N * per_row / kDzBudget) + 1;
+    if (nc > N) nc = N;
+    bp->R = std::min(round_up((N + nc - 1) / nc, 256), round_up(N, 8));
+    bp->chunks = (int)((N + bp->R - 1) / bp->R);
+  } else {
+    bp->R = 0;
+    bp->chunks = 0;
+  }
+  bp->Rp = round_up(bp->R, 8);
+  // every pass of every chunk must plan (32-bit offsets, resource sizes)
+  Plan pl;
+  int rc;
+  if (bp->R > 0) {
+    if ((rc = make_plan(bp->R, D, V, dtype, &pl)) != FLCE_OK) return rc;          // dZ
+    if ((rc = make_plan(D, bp->Vp, bp->R, dtype, &pl)) != FLCE_OK) return rc;     // dH
+    if ((rc = make_plan(D, bp->Rp, V, dtype, &pl)) != FLCE_OK) return rc;         // dW
+  }
+  if (bp->Vp * es >= (int64_t(1) << 31) || bp->Rp * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  bp->off_wt = 0;
+  bp->off_ht = align_up((size_t)(D * bp->Vp * es));
+  bp->off_dz = bp->off_ht + align_up((size_t)(D * bp->Rp * es));
+  bp->off_dzt = bp->off_dz + align_up((size_t)(bp->Rp * bp->Vp * es));
+  bp->ws_bytes = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Rp * es));
+  return FLCE_OK;
+}
+
+template <typename T>
+void launch_transpose(const void* in, int rows, int cols, int64_t ld_in, void* out, int64_t ld_out,
+                      int out_len, hipStream_t stream) {
+  const dim3 grid((unsigned)((out_len + 63) / 64), (unsigned)((cols + 63) / 64));
+  hipLaunchKernelGGL((flce_transpose_kernel<T>), grid, dim3(256), 0, stream, (const T*)in, rows, cols, ld_in,
+                     (T*)out, ld_out, out_len);
+}
+
+int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32_t* y, const float* lse,
+                    const float* grad, float* dH, float* dW, void* ws, hipStream_t stream) {
+  char* base = (char*)ws;
+  char* wt = base + bp.off_wt;
+  char* ht = base + bp.off_ht;
+  char* dz = base + bp.off_dz;
+  char* dzt = base + bp.off_dzt;
+  const bool bf = bp.dtype == FLCE_BF16;
+  // W^T: [D][Vp]
+  if (bf)
+    launch_transpose<__bf16>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
+  else
+    launch_transpose<float>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
+  for (int c = 0; c < bp.chunks; ++c) {
+    const int64_t r0 = (int64_t)c * bp.R;
+    const int64_t rc = std::min(bp.R, bp.N - r0);
+    const int64_t rcp = round_up(rc, 8);
+    const char* Hc = (const char*)H + r0 * bp.D * (int64_t)bp.es;
+    // H[chunk]^T: [D][rcp]
+    if (bf)
+      launch_transpose<__bf16>(Hc, (int)rc, (int)bp.D, bp.D, ht, rcp, (int)rcp, stream);
+    else
+      launch_transpose<float>(Hc, (int)rc, (int)bp.D, bp.D, ht, rcp, (int)rcp, stream);
+    Plan pz, ph, pw;
+    if (make_plan(rc, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK || make_plan(bp.D, bp.Vp, rc, bp.dtype, &ph) != FLCE_OK ||
+        make_plan(bp.D, rcp, bp.V, bp.dtype, &pw) != FLCE_OK)
+      return FLCE_ERR_UNSUPPORTED;
+    // dZ of the chunk
+    TileArgs a = tile_args(pz, Hc, W);
+    a.y = y + r0;
+    a.lse = lse + r0;
+    a.grad = grad + r0;
+    a.dz = dz;
+    a.dzt = dzt;
+    a.dz_ld = (int)bp.Vp;
+    a.dzt_ld = (int)rcp;
+    a.dz_rows = (int)rcp;
+    a.dz_cols = (int)bp.Vp;
+    FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
+    // dH[chunk] = dz . W: A = dz [rc][Vp], B = W^T [D][Vp]
+    TileArgs g = tile_args(ph, wt, dz);
+    g.C = dH + r0 * bp.D;
+    g.ldc = (int)bp.D;
+    g.accumulate = 0;
+    FLCE_LAUNCH_TILES(flce_gemm_kernel, ph, g, stream);
+    // dW (+)= dzt . H[chunk]: A = dzt [V][rcp], B = H[chunk]^T [D][rcp]
+    TileArgs w = tile_args(pw, ht, dzt);
+    w.C = dW;
+    w.ldc = (int)bp.D;
+    w.accumulate = c > 0;
+    FLCE_LAUNCH_TILES(flce_gemm_kernel, pw, w, stream);
+  }
+  if (bp.chunks == 0) {
+    const int64_t n = bp.V * bp.D;
+    hipLaunchKernelGGL(flce_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                       stream, dW, n);
+  }
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -770,6 +1059,28 @@ int flce_forward(const void* H, const void* W, const int32_t* targets, int64_t N
   if (rc == FLCE_OK) rc = launch_merge(pl, targets, loss_out, lse_out, ws, s);
   if (hipFreeAsync(ws, s) != hipSuccess && rc == FLCE_OK) rc = FLCE_ERR_HIP;
   return rc;
+}
+
+size_t flce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
+  BwdPlan bp;
+  if (make_bwd_plan(N, D, V, dtype, &bp) != FLCE_OK) return 0;
+  return bp.ws_bytes;
+}
+
+int flce_backward(const void* H, const void* W, const int32_t* targets, const float* lse, const float* grad_loss,
+                  int64_t N, int64_t D, int64_t V, int dtype, float* dH, float* dW, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  BwdPlan bp;
+  int rc = make_bwd_plan(N, D, V, dtype, &bp);
+  if (rc != FLCE_OK) return rc;
+  if (!W || !dW || !aligned(W, 16) || !aligned(dW, 4)) return FLCE_ERR_INVALID_ARG;
+  if (N > 0) {
+    if ((rc = check_inputs(H, W, targets, N)) != FLCE_OK) return rc;
+    if (!lse || !grad_loss || !dH || !aligned(lse, 4) || !aligned(grad_loss, 4) || !aligned(dH, 4))
+      return FLCE_ERR_INVALID_ARG;
+  }
+  if (!workspace || workspace_bytes < bp.ws_bytes || !aligned(workspace, kAlign)) return FLCE_ERR_INVALID_ARG;
+  return launch_backward(bp, H, W, targets, lse, grad_loss, dH, dW, workspace, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -138,7 +138,8 @@ def backward(H, W, y, g, rows=None, want_dW=True, lib=None):
     """Gradient of sum_i g_i loss_i: returns a dict of float64 arrays
     dH (R, D) and dH_abs for the selected rows (all rows if rows is None), and,
     when want_dW, dW (V, D) and dW_abs over all rows. The *_abs arrays are the
-    sums of absolute values of each output's terms.
+    sums of the absolute values of each output's terms, with dZ split into its
+    two terms g p and -g [v == y] (so V = 1, where dZ = 0, still has a size).
 
     g: the upstream gradient per token (float32 or float64, length N); it is
     widened exactly to float64.

@@ -141,20 +141,28 @@ int oracle_lce_forward(const void* H, const void* W, const int32_t* y,
  * Everything is float64, row by row, with the row's logits materialised; lse
  * is recomputed here (two passes, as in the forward) rather than taken from
  * anywhere else. Alongside each output the sum of the absolute values of its
- * terms is returned (dH_abs_id = sum_v |dZ_iv W_vd|, dW_abs_vd =
- * sum_i |dZ_iv H_id|), from which an error bound for a lower-precision
- * evaluation of the same sums follows.
+ * terms is returned, with dZ written as the two terms g_i p_iv and
+ * -g_i [v == y_i]: dH_abs_id = sum_v |g_i| (p_iv + [v == y_i]) |W_vd| and
+ * dW_abs_vd = sum_i |g_i| (p_iv + [v == y_i]) |H_id|. An evaluation that
+ * rounds dZ, or computes p with a small relative error, is off by at most
+ * that relative error times these sums.
  *
  * rows: R row indices for dH (NULL: all N rows, R = N). dW (and dW_abs) need
  * every row and are computed only when dW is not NULL; that keeps the N x V
  * matrix dZ in memory, so it is for small shapes.
  */
-/* dZ_i = g_i (softmax(Z_i) - onehot(y_i)) into dz[0..V). */
+/* dZ_i = g_i (softmax(Z_i) - onehot(y_i)) into dz[0..V), and the absolute
+ * size of its two terms, |g_i| (p_iv + [v == y_i]), into dzabs[0..V). */
 static void row_dz(const void* H, const void* W, const int32_t* y, const double* g,
-                   int64_t D, int64_t V, int dtype, int64_t i, double* dz) {
+                   int64_t D, int64_t V, int dtype, int64_t i, double* dz, double* dzabs) {
   const double l = row_logits_lse(H, W, D, V, dtype, i, dz);
   const int64_t t = (int64_t)y[i];
-  for (int64_t v = 0; v < V; ++v) dz[v] = g[i] * (exp(dz[v] - l) - (v == t ? 1.0 : 0.0));
+  for (int64_t v = 0; v < V; ++v) {
+    const double p = exp(dz[v] - l);
+    const double hit = v == t ? 1.0 : 0.0;
+    dz[v] = g[i] * (p - hit);
+    dzabs[v] = fabs(g[i]) * (p + hit);
+  }
 }
 
 int oracle_lce_backward(const void* H, const void* W, const int32_t* y, const double* g,
@@ -165,21 +173,26 @@ int oracle_lce_backward(const void* H, const void* W, const int32_t* y, const do
   if (!rows) R = N;
   if (N > 0 && (!H || !W || !y || !g)) return -1;
   if (R > 0 && !dH) return -1;
+  /* dZ and its term sizes for every row, when dW is wanted */
   double* dz_all = NULL;
+  double* dzabs_all = NULL;
   if (dW) {
-    dz_all = (double*)malloc((size_t)(N > 0 ? N : 1) * (size_t)V * sizeof(double));
-    if (!dz_all) return -1;
+    const size_t n = (size_t)(N > 0 ? N : 1) * (size_t)V;
+    dz_all = (double*)malloc(n * sizeof(double));
+    dzabs_all = (double*)malloc(n * sizeof(double));
+    if (!dz_all || !dzabs_all) {
+      free(dz_all);
+      free(dzabs_all);
+      return -1;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < N; ++i) row_dz(H, W, y, g, D, V, dtype, i, dz_all + i * V, dzabs_all + i * V);
   }
   int failed = 0;
-  /* dZ for every row, when dW is wanted */
-  if (dW) {
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t i = 0; i < N; ++i) row_dz(H, W, y, g, D, V, dtype, i, dz_all + i * V);
-  }
   /* dH for the selected rows */
 #pragma omp parallel
   {
-    double* z = dz_all ? NULL : (double*)malloc((size_t)V * sizeof(double));
+    double* z = dz_all ? NULL : (double*)malloc(2 * (size_t)V * sizeof(double));
     if (!dz_all && !z) {
 #pragma omp atomic write
       failed = 1;
@@ -194,13 +207,14 @@ int oracle_lce_backward(const void* H, const void* W, const int32_t* y, const do
         continue;
       }
       const double* dz = dz_all ? dz_all + i * V : z;
-      if (!dz_all) row_dz(H, W, y, g, D, V, dtype, i, z);
+      const double* dzabs = dz_all ? dzabs_all + i * V : z + V;
+      if (!dz_all) row_dz(H, W, y, g, D, V, dtype, i, z, z + V);
       for (int64_t d = 0; d < D; ++d) {
         double acc = 0.0, aabs = 0.0;
         for (int64_t v = 0; v < V; ++v) {
-          const double term = dz[v] * widen(W, dtype, v * D + d);  /* dZ_iv W_vd */
-          acc += term;
-          aabs += fabs(term);
+          const double w = widen(W, dtype, v * D + d);
+          acc += dz[v] * w;  /* dZ_iv W_vd */
+          aabs += dzabs[v] * fabs(w);
         }
         dH[r * D + d] = acc;
         if (dH_abs) dH_abs[r * D + d] = aabs;
@@ -215,9 +229,9 @@ int oracle_lce_backward(const void* H, const void* W, const int32_t* y, const do
       for (int64_t d = 0; d < D; ++d) {
         double acc = 0.0, aabs = 0.0;
         for (int64_t i = 0; i < N; ++i) {
-          const double term = dz_all[i * V + v] * widen(H, dtype, i * D + d);  /* dZ_iv H_id */
-          acc += term;
-          aabs += fabs(term);
+          const double h = widen(H, dtype, i * D + d);
+          acc += dz_all[i * V + v] * h;  /* dZ_iv H_id */
+          aabs += dzabs_all[i * V + v] * fabs(h);
         }
         dW[v * D + d] = acc;
         if (dW_abs) dW_abs[v * D + d] = aabs;
@@ -225,5 +239,6 @@ int oracle_lce_backward(const void* H, const void* W, const int32_t* y, const do
     }
   }
   free(dz_all);
+  free(dzabs_all);
   return failed ? -1 : 0;
 }

@@ -80,3 +80,71 @@ EDGE = [
 # (N, D, V) for the tile- and chunk-boundary target test, one per tile size
 BOUNDARY_SHAPES = [(512, 256, 50257), (1024, 64, 151936), (4096, 64, 65536)]
 
+
+
+# ------------------------------------------------------------------ backward
+# Tolerance for the backward, derived from its arithmetic: dZ = g p - g [v == y]
+# is rounded once to the input dtype (unit roundoff u: 2^-8 for bf16, 2^-24 for
+# fp32), and p = exp(z - lse) carries the fp32 error of z and of the forward's
+# lse (an absolute error e in z - lse is a relative error e in p; 2e-5 is
+# allowed, the bf16 forward's lse tolerance being 2e-3 and its measured errors
+# ~5e-4 at |lse| ~ 366). Then each output is an fp32 sum of K terms. With S =
+# sum over the terms of |g| (p + [v == y]) |other factor| (returned by the
+# oracle), the error is at most (u + 2e-5) * S plus, for the fp32 sum, about
+# sqrt(K) * 2^-24 * S with random rounding signs; the allowance takes four times
+# that.
+UNIT_ROUNDOFF = {torch.float32: 2.0 ** -24, torch.bfloat16: 2.0 ** -8}
+
+
+def bwd_bound(abs_sum, dtype, K):
+    u = UNIT_ROUNDOFF[dtype] + 2e-5
+    return (u + 4.0 * np.sqrt(K) * 2.0 ** -24) * np.asarray(abs_sum, dtype=np.float64) + 1e-30
+
+
+def check_bwd(got, want, abs_sum, dtype, K, what):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, f"{what}: shape {got.shape} vs {want.shape}"
+    err = np.abs(got - want)
+    bound = bwd_bound(abs_sum, dtype, K)
+    if not np.all(err <= bound):
+        i = int(np.argmax(err - bound))
+        raise AssertionError(f"{what}: element {np.unravel_index(i, got.shape)}: got {got.flat[i]!r}, "
+                             f"oracle {want.flat[i]!r}, |d|={err.flat[i]:.3e} > {bound.flat[i]:.3e}")
+    rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    return float(err.max()) if err.size else 0.0, rel
+
+
+def gpu_backward(H, W, y, g):
+    """Forward (for lse), then the backward; returns dH, dW on the host."""
+    import linear_cross_entropy_amd as flce
+    _, lse = flce.flce_forward(H, W, y)
+    dH, dW = flce.flce_backward(H, W, y, lse, g)
+    torch.cuda.synchronize()
+    return dH.cpu().numpy(), dW.cpu().numpy()
+
+
+def parity_backward(H, W, y, g, what=""):
+    """GPU backward against the oracle over every row and vocabulary entry."""
+    dH, dW = gpu_backward(H, W, y, g)
+    ref = oracle.backward(H.cpu(), W.cpu(), y.cpu(), g.cpu())
+    N, D = H.shape
+    V = W.shape[0]
+    eh, rh = check_bwd(dH, ref["dH"], ref["dH_abs"], H.dtype, V, f"{what} dH")
+    ew, rw = check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, max(N, 1), f"{what} dW")
+    return dH, dW, (eh, rh, ew, rw)
+
+
+# (N, D, V, dtype) for the backward's full-parity grid: ragged rows, ragged
+# vocabulary, partial last k-stages, several row chunks are not reachable at
+# these sizes (one chunk), each tile size of the products.
+BWD_SHAPES = [
+    (1, 8, 1, "bf16"),
+    (3, 72, 31, "bf16"),
+    (257, 64, 1000, "bf16"),
+    (300, 4104, 513, "bf16"),
+    (512, 256, 32001, "bf16"),
+    (1000, 136, 5003, "bf16"),
+    (5, 36, 300, "fp32"),
+    (257, 128, 1025, "fp32"),
+]

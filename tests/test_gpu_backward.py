@@ -1,0 +1,123 @@
+"""GPU parity of the backward (gradient of sum_i g_i loss_i wrt H and W)
+against the float64 oracle, through the C ABI.
+
+The tolerance is derived from the arithmetic (tests/parity.py: bwd_bound):
+dZ is rounded once to the input dtype, then summed in fp32; the bound is that
+rounding times the sum of the absolute values of each output's terms, which
+the oracle returns alongside every output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import BWD_SHAPES, bwd_bound, check_bwd, gpu_backward, parity_backward
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_amd  # noqa: F401
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _grad(N, seed, zeros=True):
+    gen = torch.Generator().manual_seed(seed)
+    g = torch.rand(N, generator=gen) * 2 - 0.5
+    if zeros and N > 2:
+        g[1] = 0.0
+    return g.to(torch.float32).to(DEV)
+
+
+@pytest.mark.parametrize("N,D,V,dt", BWD_SHAPES, ids=lambda v: str(v))
+def test_backward_parity(N, D, V, dt):
+    _log(f"[bwd] N={N} D={D} V={V} {dt}")
+    std = 1.0 if dt == "bf16" else 0.5
+    H, W, y = workloads.make_custom(N, D, V, dt, seed=N * 13 + V, device=DEV, h_std=std,
+                                    w_std=0.5 / math.sqrt(D) * 4)
+    g = _grad(N, seed=N + V)
+    _, _, (eh, rh, ew, rw) = parity_backward(H, W, y, g, what=f"bwd N={N} D={D} V={V} {dt}")
+    _log(f"[bwd] max |d| dH {eh:.3e} (rel {rh:.2e}), dW {ew:.3e} (rel {rw:.2e})")
+
+
+def test_backward_out_of_range_target_and_zero_grad_rows():
+    """A target outside [0, V) contributes g_i softmax(Z_i); g_i = 0 rows
+    contribute nothing."""
+    N, D, V = 64, 128, 1000
+    H, W, y = workloads.make_custom(N, D, V, "bf16", seed=5, device=DEV)
+    y[0] = -1
+    y[3] = V
+    g = _grad(N, seed=9)
+    g[5] = 0.0
+    dH, dW, _ = parity_backward(H, W, y, g, what="bwd out-of-range targets")
+    assert np.all(dH[5] == 0.0) and np.all(dH[1] == 0.0)
+
+
+def test_backward_deterministic_bits():
+    N, D, V = 512, 256, 50257
+    H, W, y = workloads.make_custom(N, D, V, "bf16", seed=17, device=DEV)
+    g = _grad(N, seed=3)
+    a = gpu_backward(H, W, y, g)
+    b = gpu_backward(H, W, y, g)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_backward_production_shape_sparse_gradient():
+    """Full production shape (N=8192, D=4096, V=151936, bf16), in the launch
+    configuration the benchmark times, with the upstream gradient nonzero on 12
+    rows only: then dW is the sum over those rows alone, which the oracle
+    computes exactly on the sub-problem, and every other row of dH is 0."""
+    w = workloads.WORKLOADS["prod_bf16"]
+    _log(f"[bwd] {w.describe()} sparse gradient")
+    H, W, y = workloads.make(w, DEV)
+    rows = np.sort(workloads.subset_rows(w.N, 12, seed=99).numpy())
+    g = torch.zeros(w.N, dtype=torch.float32)
+    g[torch.as_tensor(rows)] = torch.linspace(0.25, 1.5, len(rows))
+    g = g.to(DEV)
+    dH, dW = gpu_backward(H, W, y, g)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    ref = oracle.backward(H.cpu()[sel], W.cpu(), y.cpu()[sel], g.cpu()[sel])
+    check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, w.V, "prod dH rows")
+    others = np.setdiff1d(np.arange(w.N), rows)
+    assert np.all(dH[others] == 0.0), "rows with zero upstream gradient have nonzero dH"
+    e, rel = check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, w.N, "prod dW")
+    _log(f"[bwd] prod dW max |d| {e:.3e}, relative Frobenius error {rel:.2e}")
+
+
+def test_backward_production_shape_identities():
+    """Dense upstream gradient at the production shape: sampled rows of dH
+    against the oracle row by row, and on all of dW the identities
+    sum_v dW_v = 0 and <dH, H> = <dW, W> (both hold exactly in real arithmetic)."""
+    w = workloads.WORKLOADS["prod_bf16"]
+    H, W, y = workloads.make(w, DEV)
+    g = torch.full((w.N,), 1.0 / w.N, dtype=torch.float32, device=DEV)
+    import linear_cross_entropy_amd as flce
+    _, lse = flce.flce_forward(H, W, y)
+    dH, dW = flce.flce_backward(H, W, y, lse, g)
+    torch.cuda.synchronize()
+    rows = workloads.subset_rows(w.N, 24, seed=5).numpy()
+    ref = oracle.backward(H.cpu(), W.cpu(), y.cpu(), g.cpu(), rows=rows, want_dW=False)
+    check_bwd(dH[torch.as_tensor(rows, device=DEV)].cpu().numpy(), ref["dH"], ref["dH_abs"], H.dtype, w.V,
+              "prod dH sampled rows")
+    # sum over the vocabulary of dW vanishes up to rounding: bound it by the
+    # column sums of |dW| times the dZ rounding (each term's error is bounded
+    # by u |term|, and |dW_vd| <= sum of |terms|)
+    colsum = dW.double().sum(dim=0)
+    colabs = dW.double().abs().sum(dim=0)
+    assert bool((colsum.abs() <= 0.05 * colabs).all()), "sum_v dW_v is not ~0"
+    ip_h = float((dH.double() * H.double()).sum())
+    ip_w = float((dW.double() * W.double()).sum())
+    scale = float((dH.double() * H.double()).abs().sum())
+    assert abs(ip_h - ip_w) <= 2.0 ** -7 * scale, f"<dH,H>={ip_h} vs <dW,W>={ip_w} (scale {scale})"
+    _log(f"[bwd] prod identities: <dH,H>={ip_h:.6e} <dW,W>={ip_w:.6e}")

@@ -37,15 +37,15 @@ MUTANTS = {
     "bf16_high_half_wrong": ("(uint32_t)((const uint16_t*)base)[idx] << 16",
                              "(uint32_t)((const uint16_t*)base)[idx] << 15"),
     # backward
-    "bwd_onehot_sign": ("(exp(dz[v] - l) - (v == t ? 1.0 : 0.0))", "(exp(dz[v] - l) + (v == t ? 1.0 : 0.0))"),
-    "bwd_no_upstream": ("dz[v] = g[i] * (exp(", "dz[v] = (exp("),
-    "bwd_neighbour_target": ("(v == t ? 1.0 : 0.0)", "(v == (t + 1) % V ? 1.0 : 0.0)"),
-    "bwd_unnormalised_softmax": ("(exp(dz[v] - l) -", "(exp(dz[v]) -"),
-    "bwd_dH_transposed_W": ("dz[v] * widen(W, dtype, v * D + d);", "dz[v] * widen(W, dtype, d * V + v);"),
-    "bwd_dW_reversed_rows": ("dz_all[i * V + v] * widen(H, dtype, i * D + d);",
-                             "dz_all[i * V + v] * widen(H, dtype, (N - 1 - i) * D + d);"),
-    "bwd_dW_drop_last_row": ("for (int64_t i = 0; i < N; ++i) {\n          const double term = dz_all",
-                             "for (int64_t i = 0; i < N - 1; ++i) {\n          const double term = dz_all"),
+    "bwd_onehot_sign": ("dz[v] = g[i] * (p - hit);", "dz[v] = g[i] * (p + hit);"),
+    "bwd_no_upstream": ("dz[v] = g[i] * (p - hit);", "dz[v] = (p - hit);"),
+    "bwd_neighbour_target": ("const double hit = v == t ? 1.0 : 0.0;", "const double hit = v == (t + 1) % V ? 1.0 : 0.0;"),
+    "bwd_unnormalised_softmax": ("const double p = exp(dz[v] - l);", "const double p = exp(dz[v]);"),
+    "bwd_dH_transposed_W": ("const double w = widen(W, dtype, v * D + d);", "const double w = widen(W, dtype, d * V + v);"),
+    "bwd_dW_reversed_rows": ("const double h = widen(H, dtype, i * D + d);",
+                             "const double h = widen(H, dtype, (N - 1 - i) * D + d);"),
+    "bwd_dW_drop_last_row": ("for (int64_t i = 0; i < N; ++i) {\n          const double h",
+                             "for (int64_t i = 0; i < N - 1; ++i) {\n          const double h"),
 }
 
 
