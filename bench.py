@@ -13,6 +13,8 @@ JSON line:
                workload, on the host's cores (a reported baseline only)
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prod_bf16]
+       python bench.py --backward ...   (the backward instead: one step = one
+       flce_backward, 3 x 2*N*V*D FLOP, timed over all of its launches)
 """
 from __future__ import annotations
 
@@ -100,6 +102,101 @@ def copy_calibration(nbytes: int, reps: int):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}), flush=True)
 
 
+def cpu_baseline_backward(H, W, y, g, w, target_seconds: float, max_rows: int):
+    """The oracle's backward for a row sample (dH rows only: dW needs every row)."""
+    import oracle
+    import workloads
+    Hc, Wc, yc, gc = H.cpu(), W.cpu(), y.cpu(), g.cpu()
+    threads = oracle.num_threads()
+    probe = workloads.subset_rows(w.N, max(1, threads), seed=777).numpy()[:threads]
+    t0 = time.perf_counter()
+    oracle.backward(Hc, Wc, yc, gc, rows=probe, want_dW=False)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    rows_n = int(max(len(probe), min(max_rows, target_seconds / max(per_row, 1e-9))))
+    rows_n = max(threads, (rows_n // threads) * threads)
+    rows = workloads.subset_rows(w.N, rows_n, seed=778).numpy()
+    t0 = time.perf_counter()
+    oracle.backward(Hc, Wc, yc, gc, rows=rows, want_dW=False)
+    dt = time.perf_counter() - t0
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"dH for {len(rows)} of {w.N} rows (seeded), each recomputing a full float64 row "
+                      f"of {w.V} logits over D={w.D} and summing V*D products; dW not included; "
+                      f"{dt:.2f} s wall"}
+
+
+def bench_backward(args, w):
+    """One step = flce_backward over the workload (Z recomputed, dZ, dH, dW),
+    with the forward's lse and a mean-over-tokens upstream gradient resident."""
+    import torch
+    import linear_cross_entropy_amd as flce
+    import workloads
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
+    H, W, y = workloads.make(w, dev)
+    _, lse = flce.flce_forward(H, W, y)
+    g = torch.full((w.N,), 1.0 / w.N, dtype=torch.float32, device=dev)
+    dH = torch.empty(w.N, w.D, dtype=torch.float32, device=dev)
+    dW = torch.empty(w.V, w.D, dtype=torch.float32, device=dev)
+    ws = torch.empty(flce.flce_backward_workspace_bytes(w.N, w.D, w.V, w.dtype), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        flce.flce_backward(H, W, y, lse, g, workspace=ws, dH=dH, dW=dW, stream=stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} backward steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        flce.flce_backward(H, W, y, lse, g, workspace=ws, dH=dH, dW=dW, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    avg = sum(ms) / len(ms)
+    flops = 3 * w.flops
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / (avg * 1e-3) / 1e12
+    result = {
+        "metric": f"tokens/s + % {w.dtype} MFMA peak, fused LCE backward N={w.N} D={w.D} V={w.V}",
+        "value": w.N * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, as the forward); upstream gradient 1/N per token",
+        "config": {"workload": w.name, "N": w.N, "D": w.D, "V": w.V, "input_dtype": w.dtype,
+                   "workspace_bytes": ws.numel()},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "flce_backward (all launches: transposes, dZ pass, dH and dW products)",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "algorithmic_flop_per_launch": flops,
+            "algorithmic_bytes_per_launch": w.N * w.D * 2 + w.V * w.D * 2 + 12 * w.N + 4 * (w.N + w.V) * w.D,
+            "kernel_ms_avg": avg,
+            "kernel_ms_median": ms[len(ms) // 2],
+            "kernel_ms_min": ms[0],
+        },
+        "outputs_finite": bool(torch.isfinite(dH).all().item() and torch.isfinite(dW).all().item()),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle's backward on a row sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline_backward(H, W, y, g, w, args.cpu_seconds, args.cpu_max_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +209,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of BYTES bytes (counter scaling), then exit")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (flce_backward, given the forward's lse) instead of the forward")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -132,6 +231,9 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
+    if args.backward:
+        bench_backward(args, w)
+        return
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
     H, W, y = workloads.make(w, dev)

@@ -97,7 +97,7 @@ typedef TileCfg<384, 256, 2, 4> Tile384;
 enum TileMode {
   kForward = 0,  // online (max, sum) per token, target capture, per-chunk partials
   kDz = 1,       // dZ = g (softmax - onehot), written row-major and transposed
-  kGemm = 2,     // plain C[a][b] = Z (or C += Z)
+  kGemm = 2,     // plain C[a][b] = Z
 };
 
 struct TileArgs {
@@ -122,7 +122,7 @@ struct TileArgs {
   int dz_cols;        // vocabulary rows to write (V rounded up)
   // kGemm
   float* C;           // [V][ldc] fp32
-  int ldc, accumulate;
+  int ldc;
 };
 
 // Element-type specific pieces: a 16-byte fragment and the matrix-core step
@@ -501,7 +501,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
           }
       }
     } else {
-      // ---- C[a][b] = Z (or C += Z) for a < V, b < N
+      // ---- C[a][b] = Z for a < V, b < N
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int b = t0 + wt * WT + nb * 32 + (lane & 31);
@@ -511,10 +511,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int a = vw + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (a < p.V) {
-              float* c = p.C + (size_t)a * p.ldc + b;
-              *c = p.accumulate ? *c + acc[mb][nb][r] : acc[mb][nb][r];
-            }
+            if (a < p.V) p.C[(size_t)a * p.ldc + b] = acc[mb][nb][r];
           }
       }
     }
@@ -834,17 +831,22 @@ int launch_merge(const Plan& pl, const int32_t* y, float* loss, float* lse, cons
 }
 
 // ------------------------------------------------------------------ backward
-// The backward runs over chunks of R rows. Per chunk: the dZ pass recomputes
-// Z for the chunk (the forward's tile loop, full D) and writes
-// dZ = g (softmax - onehot) in the input dtype twice, dz[R][Vp] and
-// dzt[Vp][Rp]; then dH[chunk] = dz . W (B operand: W transposed, [D][Vp]) and
-// dW (+)= dzt . H[chunk] (B operand: the chunk of H transposed, [D][Rp]), both
-// on the same tile loop with a store epilogue. Vp and Rp round V and R up to
-// 8 elements (16-byte rows); the padding is written as zeros.
-constexpr double kDzBudget = 4.0 * 1024 * 1024 * 1024;  // bytes for dz + dzt
+// The backward runs the dZ pass and the dH product over chunks of R rows, then
+// one dW product over all rows:
+//   1. W^T ([D][Vp]) and H^T ([D][Np]): K-contiguous copies for the products.
+//   2. Per chunk: the dZ pass recomputes Z for the chunk (the forward's tile
+//      loop, full D) and writes dZ = g (softmax - onehot) in the input dtype
+//      twice: row-major for the chunk, dz[R][Vp], and into the chunk's
+//      columns of the transposed dZ of all rows, dzt[Vp][Np]; then
+//      dH[chunk] = dz . W (A = dz, B = W^T).
+//   3. dW = dzt . H (A = dzt, B = H^T), contracting over all N rows at once.
+// Vp, Np and the chunk's row count round up to 8 elements (16-byte rows); the
+// padding is written as zeros. Chunking bounds the row-major dz to about
+// kDzBudget bytes; dzt holds every row.
+constexpr double kDzBudget = 2.0 * 1024 * 1024 * 1024;
 
 struct BwdPlan {
-  int64_t N, D, V, Vp, R, Rp;
+  int64_t N, D, V, Vp, Np, R, Rp;
   int dtype, chunks;
   size_t es, off_wt, off_ht, off_dz, off_dzt, ws_bytes;
 };
@@ -863,31 +865,32 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
   bp->dtype = dtype;
   bp->es = (size_t)es;
   bp->Vp = round_up(V, 8);
+  bp->Np = round_up(N, 8);
   if (N > 0) {
-    const double per_row = 2.0 * (double)bp->Vp * (double)es;
+    const double per_row = (double)bp->Vp * (double)es;
     int64_t nc = (int64_t)((double)N * per_row / kDzBudget) + 1;
     if (nc > N) nc = N;
-    bp->R = std::min(round_up((N + nc - 1) / nc, 256), round_up(N, 8));
+    bp->R = std::min(round_up((N + nc - 1) / nc, 256), bp->Np);
     bp->chunks = (int)((N + bp->R - 1) / bp->R);
   } else {
     bp->R = 0;
     bp->chunks = 0;
   }
   bp->Rp = round_up(bp->R, 8);
-  // every pass of every chunk must plan (32-bit offsets, resource sizes)
+  // every pass must plan (32-bit offsets, resource sizes)
   Plan pl;
   int rc;
   if (bp->R > 0) {
     if ((rc = make_plan(bp->R, D, V, dtype, &pl)) != FLCE_OK) return rc;          // dZ
     if ((rc = make_plan(D, bp->Vp, bp->R, dtype, &pl)) != FLCE_OK) return rc;     // dH
-    if ((rc = make_plan(D, bp->Rp, V, dtype, &pl)) != FLCE_OK) return rc;         // dW
+    if ((rc = make_plan(D, bp->Np, V, dtype, &pl)) != FLCE_OK) return rc;         // dW
   }
-  if (bp->Vp * es >= (int64_t(1) << 31) || bp->Rp * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  if (bp->Vp * es >= (int64_t(1) << 31) || bp->Np * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
   bp->off_wt = 0;
   bp->off_ht = align_up((size_t)(D * bp->Vp * es));
-  bp->off_dz = bp->off_ht + align_up((size_t)(D * bp->Rp * es));
+  bp->off_dz = bp->off_ht + align_up((size_t)(D * bp->Np * es));
   bp->off_dzt = bp->off_dz + align_up((size_t)(bp->Rp * bp->Vp * es));
-  bp->ws_bytes = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Rp * es));
+  bp->ws_bytes = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Np * es));
   return FLCE_OK;
 }
 
@@ -901,40 +904,43 @@ void launch_transpose(const void* in, int rows, int cols, int64_t ld_in, void* o
 
 int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32_t* y, const float* lse,
                     const float* grad, float* dH, float* dW, void* ws, hipStream_t stream) {
+  if (bp.chunks == 0) {  // no rows: dW = 0
+    const int64_t n = bp.V * bp.D;
+    hipLaunchKernelGGL(flce_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
+                       stream, dW, n);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
   char* base = (char*)ws;
   char* wt = base + bp.off_wt;
   char* ht = base + bp.off_ht;
   char* dz = base + bp.off_dz;
   char* dzt = base + bp.off_dzt;
   const bool bf = bp.dtype == FLCE_BF16;
-  // W^T: [D][Vp]
-  if (bf)
+  // W^T: [D][Vp] and H^T: [D][Np]
+  if (bf) {
     launch_transpose<__bf16>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
-  else
+    launch_transpose<__bf16>(H, (int)bp.N, (int)bp.D, bp.D, ht, bp.Np, (int)bp.Np, stream);
+  } else {
     launch_transpose<float>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
+    launch_transpose<float>(H, (int)bp.N, (int)bp.D, bp.D, ht, bp.Np, (int)bp.Np, stream);
+  }
   for (int c = 0; c < bp.chunks; ++c) {
     const int64_t r0 = (int64_t)c * bp.R;
     const int64_t rc = std::min(bp.R, bp.N - r0);
-    const int64_t rcp = round_up(rc, 8);
+    const int64_t rcp = std::min(round_up(rc, 8), bp.Np - r0);
     const char* Hc = (const char*)H + r0 * bp.D * (int64_t)bp.es;
-    // H[chunk]^T: [D][rcp]
-    if (bf)
-      launch_transpose<__bf16>(Hc, (int)rc, (int)bp.D, bp.D, ht, rcp, (int)rcp, stream);
-    else
-      launch_transpose<float>(Hc, (int)rc, (int)bp.D, bp.D, ht, rcp, (int)rcp, stream);
-    Plan pz, ph, pw;
-    if (make_plan(rc, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK || make_plan(bp.D, bp.Vp, rc, bp.dtype, &ph) != FLCE_OK ||
-        make_plan(bp.D, rcp, bp.V, bp.dtype, &pw) != FLCE_OK)
+    Plan pz, ph;
+    if (make_plan(rc, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK || make_plan(bp.D, bp.Vp, rc, bp.dtype, &ph) != FLCE_OK)
       return FLCE_ERR_UNSUPPORTED;
-    // dZ of the chunk
+    // dZ of the chunk: rows [0, rcp) of dz, columns [r0, r0 + rcp) of dzt
     TileArgs a = tile_args(pz, Hc, W);
     a.y = y + r0;
     a.lse = lse + r0;
     a.grad = grad + r0;
     a.dz = dz;
-    a.dzt = dzt;
+    a.dzt = dzt + r0 * (int64_t)bp.es;
     a.dz_ld = (int)bp.Vp;
-    a.dzt_ld = (int)rcp;
+    a.dzt_ld = (int)bp.Np;
     a.dz_rows = (int)rcp;
     a.dz_cols = (int)bp.Vp;
     FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
@@ -942,20 +948,15 @@ int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32
     TileArgs g = tile_args(ph, wt, dz);
     g.C = dH + r0 * bp.D;
     g.ldc = (int)bp.D;
-    g.accumulate = 0;
     FLCE_LAUNCH_TILES(flce_gemm_kernel, ph, g, stream);
-    // dW (+)= dzt . H[chunk]: A = dzt [V][rcp], B = H[chunk]^T [D][rcp]
-    TileArgs w = tile_args(pw, ht, dzt);
-    w.C = dW;
-    w.ldc = (int)bp.D;
-    w.accumulate = c > 0;
-    FLCE_LAUNCH_TILES(flce_gemm_kernel, pw, w, stream);
   }
-  if (bp.chunks == 0) {
-    const int64_t n = bp.V * bp.D;
-    hipLaunchKernelGGL(flce_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
-                       stream, dW, n);
-  }
+  // dW = dzt . H: A = dzt [V][Np], B = H^T [D][Np]
+  Plan pw;
+  if (make_plan(bp.D, bp.Np, bp.V, bp.dtype, &pw) != FLCE_OK) return FLCE_ERR_UNSUPPORTED;
+  TileArgs w = tile_args(pw, ht, dzt);
+  w.C = dW;
+  w.ldc = (int)bp.D;
+  FLCE_LAUNCH_TILES(flce_gemm_kernel, pw, w, stream);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

@@ -121,3 +121,24 @@ def test_backward_production_shape_identities():
     scale = float((dH.double() * H.double()).abs().sum())
     assert abs(ip_h - ip_w) <= 2.0 ** -7 * scale, f"<dH,H>={ip_h} vs <dW,W>={ip_w} (scale {scale})"
     _log(f"[bwd] prod identities: <dH,H>={ip_h:.6e} <dW,W>={ip_w:.6e}")
+
+
+def test_backward_row_chunks_with_ragged_last_chunk():
+    """A shape whose dZ needs two row chunks, the second one ragged
+    (N=5000, V=262144: chunks of 2560 and 2440 rows), with the upstream
+    gradient on rows of both chunks and at the chunk edges: all of dW and the
+    gradient rows of dH against the oracle on those rows, zeros elsewhere."""
+    import linear_cross_entropy_amd as flce
+    N, D, V = 5000, 64, 262144
+    assert flce.flce_backward_workspace_bytes(N, D, V, "bf16") > 0
+    H, W, y = workloads.make_custom(N, D, V, "bf16", seed=21, device=DEV)
+    rows = np.array([0, 7, 2559, 2560, 2561, 4000, 4991, 4999])
+    g = torch.zeros(N, dtype=torch.float32)
+    g[torch.as_tensor(rows)] = torch.linspace(0.5, 1.25, len(rows))
+    g = g.to(DEV)
+    dH, dW = gpu_backward(H, W, y, g)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    ref = oracle.backward(H.cpu()[sel], W.cpu(), y.cpu()[sel], g.cpu()[sel])
+    check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, V, "two chunks dH rows")
+    assert np.all(dH[np.setdiff1d(np.arange(N), rows)] == 0.0)
+    check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, N, "two chunks dW")
