@@ -139,6 +139,51 @@ def test_invalid_arguments_rejected_before_any_launch(flce):
     assert lib.flce_forward_ws(None, None, None, 0, 8, 10, 0, None, None, None, 0, None) == flce.FLCE_OK
 
 
+def test_backward_arguments_rejected_before_any_launch(flce):
+    lib = flce._lib
+    buf = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first
+    odd = ctypes.c_void_p(4096 + 8)
+    need = flce.flce_backward_workspace_bytes(4, 8, 10, 0)
+    assert need > 0
+
+    def bwd(H=buf, W=buf, y=buf, lse=buf, g=buf, N=4, D=8, V=10, dt=0, dH=buf, dW=buf, ws=buf, nb=need):
+        return lib.flce_backward(H, W, y, lse, g, N, D, V, dt, dH, dW, ws, nb, None)
+
+    assert bwd(D=0) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(V=0) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(N=-1) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(dt=7) == flce.FLCE_ERR_UNSUPPORTED
+    assert bwd(D=12) == flce.FLCE_ERR_UNSUPPORTED          # 24 bytes per bf16 row
+    for name in ("H", "W", "y", "lse", "g", "dH", "dW", "ws"):
+        assert bwd(**{name: None}) == flce.FLCE_ERR_INVALID_ARG, name
+    assert bwd(H=odd) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(ws=odd) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(nb=need - 1) == flce.FLCE_ERR_INVALID_ARG
+
+
+def test_backward_workspace_layout(flce):
+    """The workspace holds W^T, H^T, one chunk of row-major dZ and dZ^T of all
+    rows, each rounded to 8 elements and 256-byte aligned; chunks keep the
+    row-major dZ near 2 GiB."""
+    def up(x, m):
+        return (x + m - 1) // m * m
+
+    for N, D, V, dt, es in [(4, 8, 10, 0, 2), (128, 64, 1024, 1, 4), (8192, 4096, 151936, 0, 2),
+                            (5000, 64, 262144, 0, 2), (0, 8, 10, 0, 2)]:
+        Vp, Np = up(V, 8), up(N, 8)
+        if N:
+            nc = int(N * Vp * es / 2 ** 31) + 1
+            R = min(up(-(-N // nc), 256), Np)
+        else:
+            R = 0
+        Rp = up(R, 8)
+        want = (up(D * Vp * es, 256) + up(D * Np * es, 256) + up(Rp * Vp * es, 256) + up(Vp * Np * es, 256))
+        assert flce.flce_backward_workspace_bytes(N, D, V, dt) == want, (N, D, V, dt)
+        if N:
+            assert Rp * Vp * es <= 2 ** 31 + 256 * Vp * es    # one chunk of dZ stays near the budget
+    assert flce.flce_backward_workspace_bytes(4, 12, 10, 0) == 0   # unsupported D
+
+
 def test_python_binding_validates_shapes(flce):
     import torch
     H = torch.zeros(4, 8, dtype=torch.bfloat16)
