@@ -603,26 +603,42 @@ __global__ __launch_bounds__(256) void flce_merge_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ backward helpers
 // out[c][r] = in[r][c] for c < cols and r < rows, and 0 for rows <= r < out_len:
-// the backward's K-contiguous copies of W (vocabulary along K) and of a chunk
-// of H (tokens along K). 64 x 64 tiles staged through LDS; the extra column
-// keeps the transposed LDS reads on distinct banks.
+// the backward's K-contiguous copies of W (vocabulary along K) and of H (tokens
+// along K). 64 x 64 tiles staged through LDS, moved in 16-byte vectors both
+// ways (cols, ld_in, out_len and ld_out are multiples of 16 bytes' worth of
+// elements). The LDS row is padded by 4 bytes, so the column gathers of one
+// store instruction (8 rows 8 apart x 8 columns) fall on distinct banks.
 template <typename T>
 __global__ __launch_bounds__(256) void flce_transpose_kernel(const T* __restrict__ in, int rows, int cols,
                                                              int64_t ld_in, T* __restrict__ out,
                                                              int64_t ld_out, int out_len) {
-  __shared__ T tile[64][65];
+  constexpr int E = 16 / sizeof(T);      // elements per 16-byte vector
+  constexpr int VPR = 64 / E;            // vectors per 64-element tile row
+  constexpr int PAD = 4 / sizeof(T) > 0 ? 4 / sizeof(T) : 1;
+  typedef T vec __attribute__((ext_vector_type(E)));
+  __shared__ T tile[64][64 + PAD];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-#pragma unroll 4
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    tile[i][tx] = (r < rows && c < cols) ? in[(size_t)r * ld_in + c] : (T)0.f;
+  // load: tile row i, elements [E*j, E*j + E)
+#pragma unroll
+  for (int k = threadIdx.x; k < 64 * VPR; k += 256) {
+    const int i = k / VPR, j = k % VPR;
+    const int r = r0 + i, c = c0 + E * j;
+    vec v = {};
+    if (r < rows && c < cols) v = *(const vec*)(in + (size_t)r * ld_in + c);
+#pragma unroll
+    for (int e = 0; e < E; ++e) tile[i][E * j + e] = v[e];
   }
   __syncthreads();
-#pragma unroll 4
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (c < cols && r < out_len) out[(size_t)c * ld_out + r] = tile[tx][i];
+  // store: out row c0 + i (tile column i), elements [r0 + E*j, + E)
+#pragma unroll
+  for (int k = threadIdx.x; k < 64 * VPR; k += 256) {
+    const int i = k / VPR, j = k % VPR;
+    const int c = c0 + i, r = r0 + E * j;
+    if (c >= cols || r >= out_len) continue;
+    vec v;
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = tile[E * j + e][i];
+    *(vec*)(out + (size_t)c * ld_out + r) = v;
   }
 }
 
