@@ -142,3 +142,27 @@ def test_backward_row_chunks_with_ragged_last_chunk():
     check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, V, "two chunks dH rows")
     assert np.all(dH[np.setdiff1d(np.arange(N), rows)] == 0.0)
     check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, N, "two chunks dW")
+
+
+def test_backward_stress_shape_sparse_gradient():
+    """The large-vocabulary stress workload (N=8192, D=8192, V=262144, 64
+    outlier W rows): three row chunks. Gradient on 8 rows spread over the
+    chunks; all of dW and those dH rows against the oracle on those rows."""
+    w = workloads.WORKLOADS["stress_bf16"]
+    _log(f"[bwd] {w.describe()} sparse gradient")
+    H, W, y = workloads.make(w, DEV)
+    rows = np.array([0, 1500, 2815, 2816, 5000, 5631, 5632, 8191])
+    g = torch.zeros(w.N, dtype=torch.float32)
+    g[torch.as_tensor(rows)] = torch.linspace(0.25, 2.0, len(rows))
+    g = g.to(DEV)
+    dH, dW = gpu_backward(H, W, y, g)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    ref = oracle.backward(H.cpu()[sel], W.cpu(), y.cpu()[sel], g.cpu()[sel])
+    check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, w.V, "stress dH rows")
+    assert np.all(dH[np.setdiff1d(np.arange(w.N), rows)] == 0.0)
+    worst = 0.0
+    for v0 in range(0, w.V, 16384):       # blocks of vocabulary rows keep host temporaries small
+        e, _ = check_bwd(dW[v0:v0 + 16384], ref["dW"][v0:v0 + 16384], ref["dW_abs"][v0:v0 + 16384],
+                         H.dtype, w.N, f"stress dW rows {v0}..")
+        worst = max(worst, e)
+    _log(f"[bwd] stress dW max |d| {worst:.3e}")
