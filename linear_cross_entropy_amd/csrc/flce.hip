@@ -1,11 +1,11 @@
-// Fused linear cross-entropy forward for AMD Instinct MI355X (gfx950, CDNA4).
+// Fused linear cross-entropy, forward and backward, for AMD Instinct MI355X
+// (gfx950, CDNA4).
 //
-// Computes, for H (N x D), W (V x D) and int32 targets y,
+// Forward: for H (N x D), W (V x D) and int32 targets y,
 //     lse_i  = logsumexp_v (H W^T)[i, v],     loss_i = lse_i - (H W^T)[i, y_i]
-// as defined on the page "Een gefuseerde forward-kernel
-// voor lineaire cross-entropy op Apple-GPU's" (section 1), without ever storing the N x V logits.
-//
-// Two launches on the caller's stream:
+// as defined on the page "Een gefuseerde forward-kernel voor lineaire
+// cross-entropy op Apple-GPU's" (section 1), without ever storing the N x V
+// logits. Two launches on the caller's stream:
 //   1. flce_partials_kernel: a persistent-per-CU grid over (row block, vocab
 //      chunk). Each workgroup owns BT tokens and a run of BV-row vocabulary
 //      tiles. For every tile it contracts H_blk W_tile^T over the whole of D
@@ -23,6 +23,12 @@
 // only at the end. This is the same identity the page uses between tiles
 // (combining two partial states with the max-rescaled sum), applied to a
 // different grouping of the vocabulary.
+//
+// Backward (gradients of sum_i g_i loss_i; the page's training path keeps
+// the forward's lse and regenerates the logits, section 1): the same tile
+// loop recomputes Z and writes dZ = g (softmax - onehot) (flce_dz_kernel),
+// and runs the two products dH = dZ W and dW = dZ^T H with a store epilogue
+// (flce_gemm_kernel) on K-contiguous transposed copies (flce_transpose_kernel).
 
 #include <hip/hip_runtime.h>
 
@@ -378,10 +384,10 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     FLCE_WAIT_VMCNT(0);          // this wave's loads of stage g have landed in LDS
     __syncthreads();             // ... and everyone's; stage g - 1's buffer is free
     const char* sb = smem + (g & 1) * kStageBytes;
+    if (g + 1 < total) issue((g + 1) & 1);
+    read_b(sb, 0);
 #pragma unroll
     for (int q = 0; q < kASlots; ++q) read_a(sb, q);
-    read_b(sb, 0);
-    if (g + 1 < total) issue((g + 1) & 1);
     if (ks == 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
