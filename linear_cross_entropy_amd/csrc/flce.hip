@@ -263,57 +263,70 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   for (int i = 0; i < WLOADS; ++i) w_chunk[i] = ((lane & 7) ^ swizzle(w_row0 + 8 * i + (lane >> 3))) * 16;
 #pragma unroll
   for (int i = 0; i < HLOADS; ++i) h_chunk[i] = ((lane & 7) ^ swizzle(kBV + h_row0 + 8 * i + (lane >> 3))) * 16;
-  // Byte offset of each load at k = 0, or an out-of-range offset for rows past
-  // the region (an out-of-range base stays out of range after adding k < 2^31).
+  // Byte offset of each load at k = 0 (W: in the chunk's first tile), or an
+  // out-of-range offset for rows past the region (an out-of-range base stays
+  // out of range after adding k < 2^31).
   uint32_t w_off[WLOADS], h_off[HLOADS];
-  auto set_tile = [&](int tile) {
 #pragma unroll
-    for (int i = 0; i < WLOADS; ++i) {
-      const int r = tile * kBV + w_row0 + 8 * i + (lane >> 3);
-      w_off[i] = r < w_rows ? (uint32_t)(r * p.row_bytes + w_chunk[i]) : kOutOfRange;
-    }
-  };
+  for (int i = 0; i < WLOADS; ++i) {
+    const int r = w_row0 + 8 * i + (lane >> 3);
+    w_off[i] = r < w_rows ? (uint32_t)(r * p.row_bytes + w_chunk[i]) : kOutOfRange;
+  }
 #pragma unroll
   for (int i = 0; i < HLOADS; ++i) {
     const int r = h_row0 + 8 * i + (lane >> 3);
     h_off[i] = r < h_rows ? (uint32_t)(r * p.row_bytes + h_chunk[i]) : kOutOfRange;
   }
 
+  // On the last k-stage of a row that is not a multiple of 128 bytes long,
+  // only lanes whose chunk starts inside the row may load: bit i of tail_ok
+  // (W loads, then H loads) says whether load i's chunk does.
+  constexpr int NLOADS = WLOADS + HLOADS;
+  const int tail_bytes = p.row_bytes - (KS - 1) * kStageRowBytes;
+  uint32_t tail_ok = 0;
+#pragma unroll
+  for (int i = 0; i < WLOADS; ++i) tail_ok |= (w_chunk[i] < tail_bytes ? 1u : 0u) << i;
+#pragma unroll
+  for (int i = 0; i < HLOADS; ++i) tail_ok |= (h_chunk[i] < tail_bytes ? 1u : 0u) << (WLOADS + i);
+
   int issue_tile = 0, issue_ks = 0;
-  set_tile(0);
-  // (offsets are cast explicitly: without it the host-side instantiation of
-  // this template drops the kernel's launch stub)
-  auto issue = [&](int buf) {
+  // Load i (W loads first) of the next stage into LDS buffer buf. With
+  // live == false the load reads out of range: it fills the buffer with
+  // zeros and touches no memory. (offsets are cast explicitly: without it the
+  // host-side instantiation of this template drops the kernel's launch stub)
+  auto issue_one = [&](int buf, int i, bool live) {
     const int kbyte = issue_ks * kStageRowBytes;
-    FLCE_LDS char* wdst = (FLCE_LDS char*)(smem) + buf * kStageBytes + w_row0 * kStageRowBytes;
-    FLCE_LDS char* hdst = (FLCE_LDS char*)(smem) + buf * kStageBytes + (kBV + h_row0) * kStageRowBytes;
-    if (kbyte + kStageRowBytes <= p.row_bytes) {
-#pragma unroll
-      for (int i = 0; i < WLOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (FLCE_LDS void*)(wdst + i * 8 * kStageRowBytes), 16,
-                                                 (uint32_t)(w_off[i] + kbyte), 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < HLOADS; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(h_rsrc, (FLCE_LDS void*)(hdst + i * 8 * kStageRowBytes), 16,
-                                                 (uint32_t)(h_off[i] + kbyte), 0, 0, 0);
+    const bool whole = kbyte + kStageRowBytes <= p.row_bytes;
+    const bool ok = live && (whole || ((tail_ok >> i) & 1u));
+    FLCE_LDS char* sbuf = (FLCE_LDS char*)(smem) + buf * kStageBytes;
+    if (i < WLOADS) {
+      const uint32_t off = ok ? w_off[i] + kbyte : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          w_rsrc, (FLCE_LDS void*)(sbuf + (w_row0 + 8 * i) * kStageRowBytes), 16, off, 0, 0, 0);
     } else {
-      // last, partial k-stage: chunks past the end of the row read as zero
-#pragma unroll
-      for (int i = 0; i < WLOADS; ++i) {
-        const uint32_t off = kbyte + w_chunk[i] < p.row_bytes ? w_off[i] + kbyte : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (FLCE_LDS void*)(wdst + i * 8 * kStageRowBytes), 16,
-                                                 off, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < HLOADS; ++i) {
-        const uint32_t off = kbyte + h_chunk[i] < p.row_bytes ? h_off[i] + kbyte : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(h_rsrc, (FLCE_LDS void*)(hdst + i * 8 * kStageRowBytes), 16,
-                                                 off, 0, 0, 0);
-      }
+      const int j = i - WLOADS;
+      const uint32_t off = ok ? h_off[j] + kbyte : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          h_rsrc, (FLCE_LDS void*)(sbuf + (kBV + h_row0 + 8 * j) * kStageRowBytes), 16, off, 0, 0, 0);
     }
+  };
+  // Moving to the next tile moves every W row by kBV rows: a load whose row
+  // is still inside the chunk advances by kBV rows' bytes, one past it reads
+  // out of range from then on. Only the lane's row within its 8-row load
+  // group varies per lane, and it is recomputed here rather than kept live.
+  auto issue_done = [&]() {
     if (++issue_ks == KS) {
       issue_ks = 0;
-      set_tile(++issue_tile);
+      ++issue_tile;
+      int l8 = threadIdx.x & 63;
+      asm volatile("" : "+v"(l8));
+      l8 >>= 3;
+      const uint32_t step = (uint32_t)(kBV * p.row_bytes);
+#pragma unroll
+      for (int i = 0; i < WLOADS; ++i) {
+        const int lim = w_rows - issue_tile * kBV - w_row0 - 8 * i;  // rows of load i still inside the chunk
+        w_off[i] = l8 < lim ? w_off[i] + step : kOutOfRange;
+      }
     }
   };
 
@@ -374,17 +387,24 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 
   // ---- main loop over the chunk's stages (tile-major, k-stage minor); stage g
   // lives in LDS buffer g & 1. After the barrier that publishes stage g (and
-  // retires stage g - 1), a wave reads its first fragments of stage g, issues
-  // the loads of stage g + 1 into the retired buffer, then runs the stage's
-  // four k-blocks with the next k-block's fragment reads spread between the
-  // current k-block's MFMAs.
-  issue(0);
+  // retires stage g - 1), a wave reads its first fragments of stage g, then
+  // runs the stage's four k-blocks with the next fragment reads spread between
+  // the MFMAs, and with its loads of stage g + 1 (into the retired buffer)
+  // issued one per MFMA step. Issued all at once, the 8 waves' loads stall
+  // instruction issue for a long stretch (the address path saturates); one per
+  // step, the waiting happens while the other wave on the SIMD runs MFMAs.
+  // The last stage's loads have nothing to fetch: they read out of range.
+  static_assert(NLOADS <= QN, "one load per MFMA step");
+#pragma unroll
+  for (int i = 0; i < NLOADS; ++i) issue_one(0, i, true);
+  issue_done();
   int ks = 0, tile = 0;
   for (int g = 0; g < total; ++g) {
     FLCE_WAIT_VMCNT(0);          // this wave's loads of stage g have landed in LDS
     __syncthreads();             // ... and everyone's; stage g - 1's buffer is free
     const char* sb = smem + (g & 1) * kStageBytes;
-    if (g + 1 < total) issue((g + 1) & 1);
+    const int nbuf = (g + 1) & 1;
+    const bool more = g + 1 < total;
     read_b(sb, 0);
 #pragma unroll
     for (int q = 0; q < kASlots; ++q) read_a(sb, q);
@@ -403,7 +423,9 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb & 1][nb], acc[mb][nb]);
       if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
       if (q + kASlots < QN) read_a(sb, q + kASlots);
+      if (q < NLOADS) issue_one(nbuf, q, more);  // one load of stage g + 1 per step
     }
+    issue_done();
     // keep that order: each W fragment's matrix instructions, then the reads
     // its slot (and, at a k-block's start, the idle H set) can take
 #pragma unroll
@@ -417,6 +439,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
         __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
       }
       if (q + kASlots < QN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one W fragment
+      if (q < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load of stage g + 1
     }
     if (++ks < KS) continue;
     ks = 0;
@@ -522,6 +545,8 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       }
     }
   }
+  FLCE_WAIT_VMCNT(0);  // the last stage's zero-filling loads land before the workgroup ends
+
 
   if constexpr (MODE != kForward) return;
 
