@@ -371,9 +371,12 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // Fragments: the NB H fragments of the current k-block and of the next one
   // (two sets), and a rolling window of kASlots W fragments. W fragment q of
   // a stage (q = kb*MB + mb) lives in slot q % kASlots; once the MFMAs that
-  // use it have issued, the slot receives fragment q + kASlots.
-  constexpr int kASlots = 3;
+  // use it have issued, the slot receives fragment q + kASlots, and across
+  // the stage boundary fragment j of the next stage (QN is a multiple of
+  // kASlots, so that is slot j again).
   constexpr int QN = 4 * MB;  // W fragments per stage
+  constexpr int kASlots = QN % 3 == 0 ? 3 : 4;
+  static_assert(QN % kASlots == 0 && MB >= kASlots, "rolling window");
   Frag fa[kASlots], fb[2][NB];
   auto read_a = [&](const char* sb, int q) {
     fa[q % kASlots] = *(const Frag*)(sb + (a_row + (q % MB) * 32) * kStageRowBytes + koff[q / MB]);
@@ -386,28 +389,38 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   constexpr int STEPS = NB * (sizeof(T) == 2 ? 1 : 4);  // matrix instructions per W fragment
 
   // ---- main loop over the chunk's stages (tile-major, k-stage minor); stage g
-  // lives in LDS buffer g & 1. After the barrier that publishes stage g (and
-  // retires stage g - 1), a wave reads its first fragments of stage g, then
-  // runs the stage's four k-blocks with the next fragment reads spread between
-  // the MFMAs, and with its loads of stage g + 1 (into the retired buffer)
-  // issued one per MFMA step. Issued all at once, the 8 waves' loads stall
+  // lives in LDS buffer g & 1 and takes QN MFMA steps (one W fragment each).
+  //   steps [0, QN - kASlots): MFMAs, the fragment reads kASlots steps ahead,
+  //     and this wave's remaining loads of stage g + 1 (into the other
+  //     buffer), one per step;
+  //   then the barrier: every wave's loads of stage g + 1 have landed, and
+  //     every read of stage g has been issued and waited for;
+  //   steps [QN - kASlots, QN): the last MFMAs of stage g, the first fragment
+  //     reads of stage g + 1, and the first kASlots loads of stage g + 2 into
+  //     stage g's buffer, which the barrier has just retired.
+  // So the fragments the next stage starts with are read under this stage's
+  // last MFMAs, not after the barrier with nothing to overlap, and the loads
+  // go out one per step: issued all at once, the 8 waves' loads stall
   // instruction issue for a long stretch (the address path saturates); one per
-  // step, the waiting happens while the other wave on the SIMD runs MFMAs.
-  // The last stage's loads have nothing to fetch: they read out of range.
-  static_assert(NLOADS <= QN, "one load per MFMA step");
+  // step, a wave waiting to issue leaves the SIMD to the other wave's MFMAs.
+  // Loads past the chunk's last stage read out of range (zero fill, no
+  // memory traffic).
+  static_assert(NLOADS > kASlots && NLOADS - kASlots <= QN - kASlots, "loads split over the steps");
+  // prologue: all of stage 0, the first kASlots loads of stage 1
 #pragma unroll
   for (int i = 0; i < NLOADS; ++i) issue_one(0, i, true);
   issue_done();
+#pragma unroll
+  for (int i = 0; i < kASlots; ++i) issue_one(1, i, 1 < total);
+  FLCE_WAIT_VMCNT(0);
+  __syncthreads();
+  read_b(smem, 0);
+#pragma unroll
+  for (int q = 0; q < kASlots; ++q) read_a(smem, q);
   int ks = 0, tile = 0;
   for (int g = 0; g < total; ++g) {
-    FLCE_WAIT_VMCNT(0);          // this wave's loads of stage g have landed in LDS
-    __syncthreads();             // ... and everyone's; stage g - 1's buffer is free
     const char* sb = smem + (g & 1) * kStageBytes;
-    const int nbuf = (g + 1) & 1;
-    const bool more = g + 1 < total;
-    read_b(sb, 0);
-#pragma unroll
-    for (int q = 0; q < kASlots; ++q) read_a(sb, q);
+    const char* sn = smem + ((g + 1) & 1) * kStageBytes;  // at g == total - 1: read and ignored
     if (ks == 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
@@ -416,20 +429,21 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
     }
+    const bool more1 = g + 1 < total;
 #pragma unroll
-    for (int q = 0; q < QN; ++q) {
+    for (int q = 0; q < QN - kASlots; ++q) {
       const int kb = q / MB, mb = q % MB;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb & 1][nb], acc[mb][nb]);
       if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
-      if (q + kASlots < QN) read_a(sb, q + kASlots);
-      if (q < NLOADS) issue_one(nbuf, q, more);  // one load of stage g + 1 per step
+      read_a(sb, q + kASlots);
+      if (q + kASlots < NLOADS) issue_one((g + 1) & 1, q + kASlots, more1);
     }
     issue_done();
     // keep that order: each W fragment's matrix instructions, then the reads
-    // its slot (and, at a k-block's start, the idle H set) can take
+    // its slot (and, at a k-block's start, the idle H set) can take, then a load
 #pragma unroll
-    for (int q = 0; q < QN; ++q) {
+    for (int q = 0; q < QN - kASlots; ++q) {
       const int kb = q / MB, mb = q % MB;
       if (mb == 0 && kb + 1 < 4) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
@@ -438,8 +452,33 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       } else {
         __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
       }
-      if (q + kASlots < QN) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one W fragment
-      if (q < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load of stage g + 1
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one W fragment
+      if (q + kASlots < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+    }
+    if (more1) {
+      FLCE_WAIT_VMCNT(0);      // this wave's loads of stage g + 1 have landed in LDS
+      __syncthreads();         // ... and everyone's; every read of stage g is done
+    }
+    // the last kASlots steps. In the chunk's last stage there is no barrier
+    // and the loads (zero fill) go to the other buffer, which no wave reads
+    // any more; the fragments read from it there are never used.
+    const bool more2 = g + 2 < total;
+    const int tbuf = more1 ? (g & 1) : ((g + 1) & 1);
+#pragma unroll
+    for (int j = 0; j < kASlots; ++j) {
+      const int q = QN - kASlots + j;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = Mma<T>::step(fa[j], fb[1][nb], acc[q % MB][nb]);
+      if (j == 0) read_b(sn, 0);
+      read_a(sn, j);
+      issue_one(tbuf, j, more2);
+    }
+#pragma unroll
+    for (int j = 0; j < kASlots; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
+      if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, NB + 1, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     if (++ks < KS) continue;
     ks = 0;
