@@ -741,8 +741,10 @@ constexpr TileInfo tile_info(int cost) {
   return TileInfo{C::BV, C::BT, C::THREADS, C::LDS_BYTES, cost};
 }
 // Per-logit costs from the production shape (N=8192, D=4096, V=151936):
-// 8.60, 8.14 and 7.80 ms for the same work with 256-, 320- and 384-row tiles.
-constexpr TileInfo kTiles[3] = {tile_info<Tile256>(1106), tile_info<Tile320>(1044), tile_info<Tile384>(1000)};
+// 7.29, 7.13 and 7.05 ms for the same work with 256-, 320- and 384-row tiles.
+// (Across nine shapes from N=1024 to 16384, D=1024 to 8192, V=32000 to
+// 262144, the planner's pick was the fastest tile or within 4% of it.)
+constexpr TileInfo kTiles[3] = {tile_info<Tile256>(1034), tile_info<Tile320>(1011), tile_info<Tile384>(1000)};
 
 // Chunks per row block for a tile: minimise the makespan in tile-times,
 // ceil(row_blocks*c / slots) * ceil(vocab_tiles / c); ties go to fewer chunks.
