@@ -84,6 +84,11 @@ struct TileCfg {
   static constexpr int HLOADS = HROWS / 8;
   static constexpr int STAGE_BYTES = (BV + BT) * kStageRowBytes;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
+  // Whether the younger wave of each SIMD takes issue priority around the
+  // stage barrier (see the main loop). Measured on the production shape: the
+  // 256-row tile is 3% faster with it, the 320- and 384-row tiles up to 1%
+  // faster without it.
+  static constexpr bool YOUNG_PRIO = BV == 256;
   static_assert(WV % 32 == 0 && WT % 32 == 0, "waves own whole MFMA tiles");
   static_assert(WROWS % 8 == 0 && HROWS % 8 == 0 && BV % 16 == 0, "whole 8-row loads");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
@@ -417,6 +422,12 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   read_b(smem, 0);
 #pragma unroll
   for (int q = 0; q < kASlots; ++q) read_a(smem, q);
+  // Issue priority: the older wave of each SIMD (waves 0..NW/2-1) wins
+  // arbitration by age, runs ahead and waits at the barrier while the younger
+  // one feeds the matrix core alone. With YOUNG_PRIO the younger wave takes
+  // the higher priority from the barrier through the stage's last steps (and
+  // a tile's epilogue) and drops it when the next stage's main steps begin.
+  const bool young = C::YOUNG_PRIO && wave >= C::NW / 2;
   int ks = 0, tile = 0;
   for (int g = 0; g < total; ++g) {
     const char* sb = smem + (g & 1) * kStageBytes;
@@ -430,6 +441,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
           for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
     }
     const bool more1 = g + 1 < total;
+    if (young) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int q = 0; q < QN - kASlots; ++q) {
       const int kb = q / MB, mb = q % MB;
@@ -439,7 +451,6 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       read_a(sb, q + kASlots);
       if (q + kASlots < NLOADS) issue_one((g + 1) & 1, q + kASlots, more1);
     }
-    issue_done();
     // keep that order: each W fragment's matrix instructions, then the reads
     // its slot (and, at a k-block's start, the idle H set) can take, then a load
 #pragma unroll
@@ -455,10 +466,14 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one W fragment
       if (q + kASlots < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
     }
+    // (after the ordering above: placed before it, this code lands in the
+    // middle of the ordered region and the LDS reads lose their interleaving)
+    issue_done();
     if (more1) {
       FLCE_WAIT_VMCNT(0);      // this wave's loads of stage g + 1 have landed in LDS
       __syncthreads();         // ... and everyone's; every read of stage g is done
     }
+    if (young) __builtin_amdgcn_s_setprio(1);
     // the last kASlots steps. In the chunk's last stage there is no barrier
     // and the loads (zero fill) go to the other buffer, which no wave reads
     // any more; the fragments read from it there are never used.
@@ -584,6 +599,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       }
     }
   }
+  __builtin_amdgcn_s_setprio(0);
   FLCE_WAIT_VMCNT(0);  // the last stage's zero-filling loads land before the workgroup ends
 
 
