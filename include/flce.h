@@ -139,9 +139,10 @@ int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtyp
  *     the result differs from exact arithmetic by about the unit roundoff of
  *     `dtype` times the sum of the absolute values of each output's terms.
  *   - The workspace (flce_backward_workspace_bytes, 256-byte aligned,
- *     FLCE_ERR_INVALID_ARG if smaller) holds W and H transposed, dZ of all
- *     rows transposed (V x N elements of `dtype`) and dZ of one chunk of rows
- *     row-major (chunks keep that part near 2 GiB at most). Allocates nothing.
+ *     FLCE_ERR_INVALID_ARG if smaller) holds W and H transposed and dZ of all
+ *     rows transposed (V x N elements of `dtype`, each dimension rounded up to
+ *     64); for fp32 also dZ of one chunk of rows row-major (chunks keep that
+ *     part near 2 GiB at most). Allocates nothing.
  *   - Other conventions (alignment, D * sizeof(element) % 16 == 0, stream,
  *     status codes) as for the forward.
  */

@@ -109,6 +109,7 @@ enum TileMode {
   kForward = 0,  // online (max, sum) per token, target capture, per-chunk partials
   kDz = 1,       // dZ = g (softmax - onehot), written row-major and transposed
   kGemm = 2,     // plain C[a][b] = Z
+  kGemmT = 3,    // C[b][a] = Z with B read from a [k][b] matrix (bf16 only)
 };
 
 struct TileArgs {
@@ -131,9 +132,11 @@ struct TileArgs {
   int dz_ld, dzt_ld;  // row lengths in elements (>= the valid extents; the rest is written as 0)
   int dz_rows;        // tokens to write in dz / columns in dzt (N rounded up)
   int dz_cols;        // vocabulary rows to write (V rounded up)
-  // kGemm
-  float* C;           // [V][ldc] fp32
+  // kGemm: C[a][b] at C[a * ldc + b]; kGemmT: C[b][a] at C[b * ldc + a]
+  float* C;           // fp32
   int ldc;
+  // kGemmT: B is stored transposed, B[b][k] at H[k * ldb + b] (elements); K = row_bytes / 2
+  int ldb;
 };
 
 // Element-type specific pieces: a 16-byte fragment and the matrix-core step
@@ -166,6 +169,14 @@ template <> struct Mma<float> {
 // (rows r and r+1 differ in bank half, rows 2 apart in chunk). Measured on
 // MI355X: ~247 B/clk/CU with this swizzle, ~127 with (r & 7), ~32 without.
 __device__ __forceinline__ int swizzle(int row) { return (row >> 1) & 7; }
+
+// XOR swizzle of the 32 16-byte chunks of a k-row of a transposed B stage
+// (kGemmT). In a transposing fragment read each half-wave takes the same 64
+// bytes (4 chunks, starting at a multiple of 4) from each of 4 consecutive
+// k-rows, and the rows are 512 bytes apart, i.e. on the same banks. XOR-ing
+// k-row k's chunk index with 4 (k & 3) moves the four pieces to the four
+// different 64-byte quarters of the 256 bytes the 64 banks cover.
+__device__ __forceinline__ int bswizzle(int krow) { return (krow & 3) * 4; }
 
 // Online-update state (m, s) in base 2: m is the running maximum logit and
 // s = sum_j 2^(z_j log2(e) - off(m)) with off(m) = fl(m * log2(e)), the fp32
@@ -282,6 +293,22 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     const int r = h_row0 + 8 * i + (lane >> 3);
     h_off[i] = r < h_rows ? (uint32_t)(r * p.row_bytes + h_chunk[i]) : kOutOfRange;
   }
+  // kGemmT: the B part of a stage holds 64 k-rows of kBT columns (kBT * 2
+  // bytes each) of the transposed B, in the same LDS bytes. Load j of wave w
+  // fills k-rows 2 (w * HLOADS + j) and the next one: lane l writes 16-byte
+  // slot l % 32 of k-row 2 (w * HLOADS + j) + l / 32, which holds that row's
+  // chunk (l % 32) ^ bswizzle(row). The offsets are relative to a buffer
+  // resource based at the stage's first k-row (and this block's first column),
+  // made per stage: k-rows past K fall outside it and read as zero.
+  constexpr int kBRowBytes = kBT * 2;
+  if constexpr (MODE == kGemmT) {
+    static_assert(sizeof(T) == 2 && 64 * kBRowBytes == kBT * kStageRowBytes, "transposed B: bf16, 64 k-rows a stage");
+#pragma unroll
+    for (int i = 0; i < HLOADS; ++i) {
+      const int krow = 2 * (wave * HLOADS + i) + (lane >> 5);
+      h_off[i] = (uint32_t)(krow * p.ldb * 2 + (((lane & 31) ^ bswizzle(krow)) * 16));
+    }
+  }
 
   // On the last k-stage of a row that is not a multiple of 128 bytes long,
   // only lanes whose chunk starts inside the row may load: bit i of tail_ok
@@ -295,6 +322,14 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   for (int i = 0; i < HLOADS; ++i) tail_ok |= (h_chunk[i] < tail_bytes ? 1u : 0u) << (WLOADS + i);
 
   int issue_tile = 0, issue_ks = 0;
+  // kGemmT: the resource for the transposed B of the stage being issued
+  auto b_stage_rsrc = [&](int ks) {
+    const int k0 = ks * 64;
+    const int krows = min(64, p.row_bytes / 2 - k0);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(p.H + ((size_t)k0 * p.ldb + t0) * 2), (short)0,
+                                             max(krows * p.ldb - t0, 0) * 2, kRsrcWord3);
+  };
+  __amdgpu_buffer_rsrc_t bt_rsrc = b_stage_rsrc(0);
   // Load i (W loads first) of the next stage into LDS buffer buf. With
   // live == false the load reads out of range: it fills the buffer with
   // zeros and touches no memory. (offsets are cast explicitly: without it the
@@ -308,6 +343,11 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       const uint32_t off = ok ? w_off[i] + kbyte : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           w_rsrc, (FLCE_LDS void*)(sbuf + (w_row0 + 8 * i) * kStageRowBytes), 16, off, 0, 0, 0);
+    } else if constexpr (MODE == kGemmT) {
+      const int j = i - WLOADS;
+      const uint32_t off = live ? h_off[j] : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          bt_rsrc, (FLCE_LDS void*)(sbuf + (kBV + h_row0 + 8 * j) * kStageRowBytes), 16, off, 0, 0, 0);
     } else {
       const int j = i - WLOADS;
       const uint32_t off = ok ? h_off[j] + kbyte : kOutOfRange;
@@ -320,6 +360,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // out of range from then on. Only the lane's row within its 8-row load
   // group varies per lane, and it is recomputed here rather than kept live.
   auto issue_done = [&]() {
+    if constexpr (MODE == kGemmT) bt_rsrc = b_stage_rsrc(issue_ks + 1 == KS ? 0 : issue_ks + 1);
     if (++issue_ks == KS) {
       issue_ks = 0;
       ++issue_tile;
@@ -382,14 +423,48 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   constexpr int QN = 4 * MB;  // W fragments per stage
   constexpr int kASlots = QN % 3 == 0 ? 3 : 4;
   static_assert(QN % kASlots == 0 && MB >= kASlots, "rolling window");
-  Frag fa[kASlots], fb[2][NB];
+  // kGemmT keeps all four k-blocks' B fragments of a stage (see the main loop)
+  constexpr bool kTB = MODE == kGemmT;
+  constexpr int kBSets = kTB ? 4 : 2;
+  Frag fa[kASlots], fb[kBSets][NB];
   auto read_a = [&](const char* sb, int q) {
     fa[q % kASlots] = *(const Frag*)(sb + (a_row + (q % MB) * 32) * kStageRowBytes + koff[q / MB]);
   };
-  auto read_b = [&](const char* sb, int kb) {
+  // kGemmT: a B fragment (column n = lane % 32, k = 8 (lane / 32) + 0..7) is
+  // two transposing reads of 4 k each. Within a 16-lane group, lane s names
+  // k-row k0 + s / 4 and columns n0 + 4 (s % 4) .. + 3, and lane s receives
+  // column n0 + s of k-rows k0 .. k0 + 3; boff[nb][h] is that address for the
+  // lane (k0 = 8 (lane / 32) + 4h at k-block 0, n0 = 16 ((lane / 16) % 2)).
+  int boff[NB][2];
+  if constexpr (MODE == kGemmT) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      fb[kb & 1][nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = 8 * (lane >> 5) + ((lane & 15) >> 2) + 4 * h;
+        const int n = wt * WT + nb * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        boff[nb][h] = kBV * kStageRowBytes + k * kBRowBytes + (((n >> 3) ^ bswizzle(k)) << 4) + (n & 7) * 2;
+      }
+  }
+  auto read_b = [&](const char* sb, int kb) {
+    if constexpr (MODE == kGemmT) {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      FLCE_LDS const char* lb = (FLCE_LDS const char*)smem + (sb - smem);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FLCE_LDS s16x4*)(lb + boff[nb][0] + kb * 16 * kBRowBytes));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (FLCE_LDS s16x4*)(lb + boff[nb][1] + kb * 16 * kBRowBytes));
+        const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        fb[kb % kBSets][nb] = __builtin_bit_cast(Frag, v);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        fb[kb % kBSets][nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
+    }
   };
   constexpr int STEPS = NB * (sizeof(T) == 2 ? 1 : 4);  // matrix instructions per W fragment
 
@@ -411,12 +486,15 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // Loads past the chunk's last stage read out of range (zero fill, no
   // memory traffic).
   static_assert(NLOADS > kASlots && NLOADS - kASlots <= QN - kASlots, "loads split over the steps");
+  static_assert(!kTB || (NLOADS + 1) / 2 <= QN - kASlots, "transposed B: two loads a step");
   // prologue: all of stage 0, the first kASlots loads of stage 1
 #pragma unroll
   for (int i = 0; i < NLOADS; ++i) issue_one(0, i, true);
   issue_done();
+  if constexpr (!kTB) {
 #pragma unroll
-  for (int i = 0; i < kASlots; ++i) issue_one(1, i, 1 < total);
+    for (int i = 0; i < kASlots; ++i) issue_one(1, i, 1 < total);
+  }
   FLCE_WAIT_VMCNT(0);
   __syncthreads();
   read_b(smem, 0);
@@ -446,17 +524,34 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     for (int q = 0; q < QN - kASlots; ++q) {
       const int kb = q / MB, mb = q % MB;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb & 1][nb], acc[mb][nb]);
-      if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb % kBSets][nb], acc[mb][nb]);
+      if constexpr (kTB) {
+        if (q == 0) {
+          read_b(sb, 1);
+          read_b(sb, 2);
+          read_b(sb, 3);
+        }
+      } else {
+        if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
+      }
       read_a(sb, q + kASlots);
-      if (q + kASlots < NLOADS) issue_one((g + 1) & 1, q + kASlots, more1);
+      if constexpr (kTB) {
+        if (2 * q < NLOADS) issue_one((g + 1) & 1, 2 * q, more1);
+        if (2 * q + 1 < NLOADS) issue_one((g + 1) & 1, 2 * q + 1, more1);
+      } else {
+        if (q + kASlots < NLOADS) issue_one((g + 1) & 1, q + kASlots, more1);
+      }
     }
     // keep that order: each W fragment's matrix instructions, then the reads
     // its slot (and, at a k-block's start, the idle H set) can take, then a load
 #pragma unroll
     for (int q = 0; q < QN - kASlots; ++q) {
       const int kb = q / MB, mb = q % MB;
-      if (mb == 0 && kb + 1 < 4) {
+      if (kTB && q == 0) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 6 * NB, 0);      // k-blocks 1-3 of B (two reads each)
+        __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
+      } else if (!kTB && mb == 0 && kb + 1 < 4) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);          // next k-block's H fragments
         __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
@@ -464,7 +559,10 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
         __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one W fragment
-      if (q + kASlots < NLOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one load
+      if (kTB && 2 * q + 1 < NLOADS)
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // two loads
+      else if (kTB ? 2 * q < NLOADS : q + kASlots < NLOADS)
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // one load
     }
     // (after the ordering above: placed before it, this code lands in the
     // middle of the ordered region and the LDS reads lose their interleaving)
@@ -483,17 +581,17 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     for (int j = 0; j < kASlots; ++j) {
       const int q = QN - kASlots + j;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = Mma<T>::step(fa[j], fb[1][nb], acc[q % MB][nb]);
+      for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = Mma<T>::step(fa[j], fb[3 % kBSets][nb], acc[q % MB][nb]);
       if (j == 0) read_b(sn, 0);
       read_a(sn, j);
-      issue_one(tbuf, j, more2);
+      if constexpr (!kTB) issue_one(tbuf, j, more2);
     }
 #pragma unroll
     for (int j = 0; j < kASlots; ++j) {
       __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
-      if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, NB + 1, 0);
+      if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, (kTB ? 2 * NB : NB) + 1, 0);
       else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if constexpr (!kTB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     if (++ks < KS) continue;
     ks = 0;
@@ -580,7 +678,25 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
               q[j] = (T)d;
               *(T*)(p.dzt + ((size_t)v * p.dzt_ld + tok) * sizeof(T)) = q[j];
             }
-            store4(p.dz + ((size_t)tok * p.dz_ld + v0) * sizeof(T), q);
+            if (p.dz) store4(p.dz + ((size_t)tok * p.dz_ld + v0) * sizeof(T), q);
+          }
+      }
+    } else if constexpr (MODE == kGemmT) {
+      // ---- C[b][a] = Z for a < V, b < N: four consecutive a per lane and
+      // register group, one 16-byte store each
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int b = t0 + wt * WT + nb * 32 + (lane & 31);
+        if (b >= p.N) continue;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int a0 = vw + mb * 32 + 8 * r4 + 4 * (lane >> 5);
+            if (a0 >= p.V) continue;
+            const float q[4] = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2],
+                                acc[mb][nb][4 * r4 + 3]};
+            store4((char*)(p.C + (size_t)b * p.ldc + a0), q);
           }
       }
     } else {
@@ -659,6 +775,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_dz_kernel(TileArgs p) {
 template <typename T, typename C>
 __global__ __launch_bounds__(C::THREADS, 1) void flce_gemm_kernel(TileArgs p) {
   tile_loop<T, C, kGemm>(p);
+}
+
+template <typename T, typename C>
+__global__ __launch_bounds__(C::THREADS, 1) void flce_gemmt_kernel(TileArgs p) {
+  tile_loop<T, C, kGemmT>(p);
 }
 
 // Merge: one thread per token, in double precision (a handful of operations
@@ -787,18 +908,18 @@ int best_chunks(int64_t row_blocks, int64_t vocab_tiles, int64_t BV, int64_t row
 // tile whose makespan (tile-times x logits per tile x cost per logit) is
 // smallest. FLCE_TILE=256, 320 or 384 in the environment forces a bf16
 // configuration (for tests and tuning; every configuration computes the same
-// result).
-int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype) {
+// result). No tile above max_tile is chosen (forced ones included).
+int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype, int max_tile) {
   if (dtype != FLCE_BF16) return kTile256;
   static const int forced = [] {
     const char* e = getenv("FLCE_TILE");
     const int v = e ? atoi(e) : 0;
     return v == 256 ? kTile256 : v == 320 ? kTile320 : v == 384 ? kTile384 : -1;
   }();
-  if (forced >= 0) return forced;
+  if (forced >= 0) return std::min(forced, max_tile);
   int best = kTile256;
   double best_t = 0;
-  for (int t = kTile256; t <= kTile384; ++t) {
+  for (int t = kTile256; t <= max_tile; ++t) {
     const TileInfo& ti = kTiles[t];
     int64_t makespan = 0;
     if (best_chunks((N + ti.BT - 1) / ti.BT, (V + ti.BV - 1) / ti.BV, ti.BV, row_bytes, &makespan) == 0) continue;
@@ -811,13 +932,13 @@ int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype) {
   return best;
 }
 
-int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl) {
+int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl, int max_tile = kTile384) {
   if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
   if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   const int64_t rb = D * es;
   if (rb % 16 != 0) return FLCE_ERR_UNSUPPORTED;
-  pl->tile = choose_tile(N, V, rb, dtype);
+  pl->tile = choose_tile(N, V, rb, dtype, max_tile);
   const TileInfo& ti = kTiles[pl->tile];
   const int kBV = ti.BV, kBT = ti.BT;
   pl->BV = kBV;
@@ -913,6 +1034,16 @@ TileArgs tile_args(const Plan& pl, const void* B, const void* A) {
       hipLaunchKernelGGL((KERNEL<__bf16, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args); \
   } while (0)
 
+// The transposed-B product: bf16 only, and at most the 320-row tile (its four
+// sets of B fragments do not fit the 384-row tile's registers).
+#define FLCE_LAUNCH_TILES_GEMMT(KERNEL, pl, args, stream)                                               \
+  do {                                                                                                  \
+    if ((pl).tile == kTile320)                                                                          \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile320>), dim3((pl).grid), dim3(Tile320::THREADS), 0, stream, args); \
+    else                                                                                                \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args); \
+  } while (0)
+
 int launch_partials(const Plan& pl, const void* H, const void* W, const int32_t* y, void* ws,
                     hipStream_t stream) {
   TileArgs a = tile_args(pl, H, W);
@@ -935,18 +1066,20 @@ int launch_merge(const Plan& pl, const int32_t* y, float* loss, float* lse, cons
 }
 
 // ------------------------------------------------------------------ backward
-// The backward runs the dZ pass and the dH product over chunks of R rows, then
-// one dW product over all rows:
+// bf16:
 //   1. W^T ([D][Vp]) and H^T ([D][Np]): K-contiguous copies for the products.
-//   2. Per chunk: the dZ pass recomputes Z for the chunk (the forward's tile
-//      loop, full D) and writes dZ = g (softmax - onehot) in the input dtype
-//      twice: row-major for the chunk, dz[R][Vp], and into the chunk's
-//      columns of the transposed dZ of all rows, dzt[Vp][Np]; then
-//      dH[chunk] = dz . W (A = dz, B = W^T).
-//   3. dW = dzt . H (A = dzt, B = H^T), contracting over all N rows at once.
-// Vp, Np and the chunk's row count round up to 8 elements (16-byte rows); the
-// padding is written as zeros. Chunking bounds the row-major dz to about
-// kDzBudget bytes; dzt holds every row.
+//   2. The dZ pass recomputes Z (the forward's tile loop, full D) for all rows
+//      and writes dZ = g (softmax - onehot) in bf16, transposed: dzt[Vp][Np].
+//   3. dH = dZ . W as C[token][d] with A = W^T and B = dZ read from dzt
+//      through transposing LDS reads (flce_gemmt_kernel): no row-major dZ.
+//   4. dW = dzt . H (A = dzt, B = H^T), contracting over all N rows.
+// fp32 (no transposing reads for 32-bit elements): the dZ pass and the dH
+// product run over chunks of R rows; the dZ pass also writes the chunk's
+// row-major dz[R][Vp], and dH[chunk] = dz . W (A = dz, B = W^T); chunking
+// bounds that row-major dz to about kDzBudget bytes.
+// Vp, Np and the chunk's row count round up to 64 elements, so that the rows
+// of the transposed copies start on 128-byte lines; the padding is written as
+// zeros.
 constexpr double kDzBudget = 2.0 * 1024 * 1024 * 1024;
 
 struct BwdPlan {
@@ -968,9 +1101,15 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
   bp->V = V;
   bp->dtype = dtype;
   bp->es = (size_t)es;
-  bp->Vp = round_up(V, 8);
-  bp->Np = round_up(N, 8);
-  if (N > 0) {
+  bp->Vp = round_up(V, 64);
+  bp->Np = round_up(N, 64);
+  if (dtype == FLCE_BF16) {
+    // one pass over all rows, no row-major dZ; a stage of the transposed B
+    // (64 k-rows of dzt) stays under 2^31 bytes
+    if (bp->Np * 2 * 64 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+    bp->R = N;
+    bp->chunks = N > 0 ? 1 : 0;
+  } else if (N > 0) {
     const double per_row = (double)bp->Vp * (double)es;
     int64_t nc = (int64_t)((double)N * per_row / kDzBudget) + 1;
     if (nc > N) nc = N;
@@ -986,14 +1125,18 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
   int rc;
   if (bp->R > 0) {
     if ((rc = make_plan(bp->R, D, V, dtype, &pl)) != FLCE_OK) return rc;          // dZ
-    if ((rc = make_plan(D, bp->Vp, bp->R, dtype, &pl)) != FLCE_OK) return rc;     // dH
+    if (dtype == FLCE_BF16) {
+      if ((rc = make_plan(N, bp->Vp, D, dtype, &pl, kTile320)) != FLCE_OK) return rc;  // dH (transposed B)
+    } else {
+      if ((rc = make_plan(D, bp->Vp, bp->R, dtype, &pl)) != FLCE_OK) return rc;   // dH
+    }
     if ((rc = make_plan(D, bp->Np, V, dtype, &pl)) != FLCE_OK) return rc;         // dW
   }
   if (bp->Vp * es >= (int64_t(1) << 31) || bp->Np * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
   bp->off_wt = 0;
   bp->off_ht = align_up((size_t)(D * bp->Vp * es));
   bp->off_dz = bp->off_ht + align_up((size_t)(D * bp->Np * es));
-  bp->off_dzt = bp->off_dz + align_up((size_t)(bp->Rp * bp->Vp * es));
+  bp->off_dzt = bp->off_dz + (dtype == FLCE_BF16 ? 0 : align_up((size_t)(bp->Rp * bp->Vp * es)));
   bp->ws_bytes = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Np * es));
   return FLCE_OK;
 }
@@ -1028,10 +1171,33 @@ int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32
     launch_transpose<float>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
     launch_transpose<float>(H, (int)bp.N, (int)bp.D, bp.D, ht, bp.Np, (int)bp.Np, stream);
   }
-  for (int c = 0; c < bp.chunks; ++c) {
+  if (bf) {
+    // dZ of all rows, transposed only
+    Plan pz, ph;
+    if (make_plan(bp.N, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK ||
+        make_plan(bp.N, bp.Vp, bp.D, bp.dtype, &ph, kTile320) != FLCE_OK)
+      return FLCE_ERR_UNSUPPORTED;
+    TileArgs a = tile_args(pz, H, W);
+    a.y = y;
+    a.lse = lse;
+    a.grad = grad;
+    a.dz = nullptr;
+    a.dzt = dzt;
+    a.dzt_ld = (int)bp.Np;
+    a.dz_rows = (int)bp.Np;
+    a.dz_cols = (int)bp.Vp;
+    FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
+    // dH[token][d] = sum_v dZ[token][v] W[v][d]: A = W^T [D][Vp], B = dZ read from dzt [Vp][Np]
+    TileArgs g = tile_args(ph, dzt, wt);
+    g.ldb = (int)bp.Np;
+    g.C = dH;
+    g.ldc = (int)bp.D;
+    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, ph, g, stream);
+  }
+  for (int c = 0; c < (bf ? 0 : bp.chunks); ++c) {
     const int64_t r0 = (int64_t)c * bp.R;
     const int64_t rc = std::min(bp.R, bp.N - r0);
-    const int64_t rcp = std::min(round_up(rc, 8), bp.Np - r0);
+    const int64_t rcp = std::min(round_up(rc, 64), bp.Np - r0);
     const char* Hc = (const char*)H + r0 * bp.D * (int64_t)bp.es;
     Plan pz, ph;
     if (make_plan(rc, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK || make_plan(bp.D, bp.Vp, rc, bp.dtype, &ph) != FLCE_OK)

@@ -123,31 +123,33 @@ def test_backward_production_shape_identities():
     _log(f"[bwd] prod identities: <dH,H>={ip_h:.6e} <dW,W>={ip_w:.6e}")
 
 
-def test_backward_row_chunks_with_ragged_last_chunk():
-    """A shape whose dZ needs two row chunks, the second one ragged
-    (N=5000, V=262144: chunks of 2560 and 2440 rows), with the upstream
-    gradient on rows of both chunks and at the chunk edges: all of dW and the
-    gradient rows of dH against the oracle on those rows, zeros elsewhere."""
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_ragged_rows_and_row_chunks(dtype):
+    """N=5000, V=262144 with the upstream gradient on a few rows (the others
+    must get dH = 0). bf16 runs one pass over all rows and reads dZ^T
+    transposed for dH; fp32 runs three row chunks of the row-major dZ (1792,
+    1792 and 1416 rows), and the gradient rows sit on every chunk edge. All of
+    dW and the gradient rows of dH against the oracle on those rows."""
     import linear_cross_entropy_amd as flce
     N, D, V = 5000, 64, 262144
-    assert flce.flce_backward_workspace_bytes(N, D, V, "bf16") > 0
-    H, W, y = workloads.make_custom(N, D, V, "bf16", seed=21, device=DEV)
-    rows = np.array([0, 7, 2559, 2560, 2561, 4000, 4991, 4999])
+    assert flce.flce_backward_workspace_bytes(N, D, V, dtype) > 0
+    H, W, y = workloads.make_custom(N, D, V, dtype, seed=21, device=DEV)
+    rows = np.array([0, 7, 1791, 1792, 2559, 2560, 3583, 3584, 4991, 4999])
     g = torch.zeros(N, dtype=torch.float32)
     g[torch.as_tensor(rows)] = torch.linspace(0.5, 1.25, len(rows))
     g = g.to(DEV)
     dH, dW = gpu_backward(H, W, y, g)
     sel = torch.as_tensor(rows, dtype=torch.long)
     ref = oracle.backward(H.cpu()[sel], W.cpu(), y.cpu()[sel], g.cpu()[sel])
-    check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, V, "two chunks dH rows")
+    check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, V, f"{dtype} dH rows")
     assert np.all(dH[np.setdiff1d(np.arange(N), rows)] == 0.0)
-    check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, N, "two chunks dW")
+    check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, N, f"{dtype} dW")
 
 
 def test_backward_stress_shape_sparse_gradient():
     """The large-vocabulary stress workload (N=8192, D=8192, V=262144, 64
-    outlier W rows): three row chunks. Gradient on 8 rows spread over the
-    chunks; all of dW and those dH rows against the oracle on those rows."""
+    outlier W rows). Gradient on 8 rows spread over the batch; all of dW and
+    those dH rows against the oracle on those rows."""
     w = workloads.WORKLOADS["stress_bf16"]
     _log(f"[bwd] {w.describe()} sparse gradient")
     H, W, y = workloads.make(w, DEV)

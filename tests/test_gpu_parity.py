@@ -166,6 +166,19 @@ def test_permuted_vocabulary():
     check_close(s1, s0.astype(np.float64), torch.bfloat16, "permuted lse")
 
 
+def test_rows_are_independent():
+    """A row's loss and lse do not depend on the other rows of the batch: a
+    prefix and a slice from the middle, run as batches of their own (other row
+    blocks, other chunk splits), agree with the full batch's rows."""
+    N, D, V = 1100, 512, 20000
+    H, W, y = workloads.make_custom(N, D, V, "bf16", seed=12, device=DEV)
+    l0, s0 = gpu_forward(H, W, y)
+    for a, b in ((0, 300), (517, 889)):
+        l1, s1 = gpu_forward(H[a:b].contiguous(), W, y[a:b].contiguous())
+        check_close(l1, l0[a:b].astype(np.float64), torch.bfloat16, f"rows [{a}, {b}) loss")
+        check_close(s1, s0[a:b].astype(np.float64), torch.bfloat16, f"rows [{a}, {b}) lse")
+
+
 def test_nan_input_propagates_to_its_row_only():
     N, D, V = 16, 64, 700
     H, W, y = workloads.make_custom(N, D, V, "fp32", seed=2, device=DEV)
