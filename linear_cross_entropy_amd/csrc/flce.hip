@@ -27,8 +27,10 @@
 // Backward (gradients of sum_i g_i loss_i; the page's training path keeps
 // the forward's lse and regenerates the logits, section 1): the same tile
 // loop recomputes Z and writes dZ = g (softmax - onehot) (flce_dz_kernel),
-// and runs the two products dH = dZ W and dW = dZ^T H with a store epilogue
-// (flce_gemm_kernel) on K-contiguous transposed copies (flce_transpose_kernel).
+// and runs the two products dW = dZ^T H with a store epilogue
+// (flce_gemm_kernel) on K-contiguous transposed copies (flce_transpose_kernel)
+// and dH = dZ W, for bf16 reading dZ from its transposed copy through
+// transposing LDS reads (flce_gemmt_kernel).
 
 #include <hip/hip_runtime.h>
 
