@@ -131,7 +131,8 @@ int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtyp
  * the same H, W and targets, and Z is recomputed, never stored whole.
  *
  *   - dH (N x D) and dW (V x D) are float32 DEVICE outputs, row-major, fully
- *     overwritten (N == 0 writes dW = 0 and reads nothing else).
+ *     overwritten (N == 0 writes dW = 0 and reads nothing else); dH must be
+ *     16-byte aligned, dW 4-byte aligned.
  *   - A target outside [0, V) matches no vocabulary row: that row contributes
  *     g_i softmax(Z_i), the gradient of its lse alone. Pass g_i = 0 to leave a
  *     row out.
@@ -142,7 +143,10 @@ int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtyp
  *     FLCE_ERR_INVALID_ARG if smaller) holds W and H transposed and dZ of all
  *     rows transposed (V x N elements of `dtype`, each dimension rounded up to
  *     64); for fp32 also dZ of one chunk of rows row-major (chunks keep that
- *     part near 2 GiB at most). Allocates nothing.
+ *     part near 2 GiB at most); for bf16 shapes whose dH product alone would
+ *     leave compute units idle, also S x N x D float32 partial sums of dH
+ *     (2 <= S <= 16 slices of the vocabulary, added in slice order, so the
+ *     result is still deterministic). Allocates nothing.
  *   - Other conventions (alignment, D * sizeof(element) % 16 == 0, stream,
  *     status codes) as for the forward.
  */

@@ -139,6 +139,10 @@ struct TileArgs {
   int ldc;
   // kGemmT: B is stored transposed, B[b][k] at H[k * ldb + b] (elements); K = row_bytes / 2
   int ldb;
+  // kGemmT split over K: the grid is ksplit copies of the row_blocks x chunks
+  // grid, copy s contracting k-stages [s * ks_per, (s + 1) * ks_per) and
+  // writing its partial C to C + s * N * ldc
+  int ksplit, ks_per;
 };
 
 // Element-type specific pieces: a 16-byte fragment and the matrix-core step
@@ -239,7 +243,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // XCD's L2 sees few distinct H blocks and W tiles at a time.
   int rb, ch;
   {
-    const int b = blockIdx.x;
+    const int b = MODE == kGemmT ? (int)blockIdx.x % (p.row_blocks * p.chunks) : (int)blockIdx.x;
     if (p.xcd_rows > 0) {
       const int x = b & 7, j = b >> 3;
       const int groups_c = p.chunks / p.xcd_chunks;
@@ -255,7 +259,13 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   const int rem_tiles = p.vocab_tiles % p.chunks;
   const int tile_begin = ch * base_tiles + min(ch, rem_tiles);
   const int ntiles = base_tiles + (ch < rem_tiles ? 1 : 0);
-  const int KS = (p.row_bytes + kStageRowBytes - 1) / kStageRowBytes;
+  const int KS_all = (p.row_bytes + kStageRowBytes - 1) / kStageRowBytes;
+  int kslice = 0, kfirst = 0, KS = KS_all;  // this workgroup's k-stages: [kfirst, kfirst + KS)
+  if constexpr (MODE == kGemmT) {
+    kslice = (int)blockIdx.x / (p.row_blocks * p.chunks);
+    kfirst = kslice * p.ks_per;
+    KS = min(p.ks_per, KS_all - kfirst);
+  }
   const int total = ntiles * KS;
 
   // ---- load plan. Each stage holds kBV W rows (LDS rows [0, kBV)) and kBT H
@@ -316,7 +326,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // only lanes whose chunk starts inside the row may load: bit i of tail_ok
   // (W loads, then H loads) says whether load i's chunk does.
   constexpr int NLOADS = WLOADS + HLOADS;
-  const int tail_bytes = p.row_bytes - (KS - 1) * kStageRowBytes;
+  const int tail_bytes = p.row_bytes - (KS_all - 1) * kStageRowBytes;
   uint32_t tail_ok = 0;
 #pragma unroll
   for (int i = 0; i < WLOADS; ++i) tail_ok |= (w_chunk[i] < tail_bytes ? 1u : 0u) << i;
@@ -331,13 +341,13 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)(p.H + ((size_t)k0 * p.ldb + t0) * 2), (short)0,
                                              max(krows * p.ldb - t0, 0) * 2, kRsrcWord3);
   };
-  __amdgpu_buffer_rsrc_t bt_rsrc = b_stage_rsrc(0);
+  __amdgpu_buffer_rsrc_t bt_rsrc = b_stage_rsrc(kfirst);
   // Load i (W loads first) of the next stage into LDS buffer buf. With
   // live == false the load reads out of range: it fills the buffer with
   // zeros and touches no memory. (offsets are cast explicitly: without it the
   // host-side instantiation of this template drops the kernel's launch stub)
   auto issue_one = [&](int buf, int i, bool live) {
-    const int kbyte = issue_ks * kStageRowBytes;
+    const int kbyte = (kfirst + issue_ks) * kStageRowBytes;
     const bool whole = kbyte + kStageRowBytes <= p.row_bytes;
     const bool ok = live && (whole || ((tail_ok >> i) & 1u));
     FLCE_LDS char* sbuf = (FLCE_LDS char*)(smem) + buf * kStageBytes;
@@ -362,7 +372,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // out of range from then on. Only the lane's row within its 8-row load
   // group varies per lane, and it is recomputed here rather than kept live.
   auto issue_done = [&]() {
-    if constexpr (MODE == kGemmT) bt_rsrc = b_stage_rsrc(issue_ks + 1 == KS ? 0 : issue_ks + 1);
+    if constexpr (MODE == kGemmT) bt_rsrc = b_stage_rsrc(kfirst + (issue_ks + 1 == KS ? 0 : issue_ks + 1));
     if (++issue_ks == KS) {
       issue_ks = 0;
       ++issue_tile;
@@ -698,7 +708,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
             if (a0 >= p.V) continue;
             const float q[4] = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2],
                                 acc[mb][nb][4 * r4 + 3]};
-            store4((char*)(p.C + (size_t)b * p.ldc + a0), q);
+            store4((char*)(p.C + ((size_t)kslice * p.N + b) * p.ldc + a0), q);
           }
       }
     } else {
@@ -854,6 +864,17 @@ __global__ __launch_bounds__(256) void flce_transpose_kernel(const T* __restrict
 // dst[0..n) = 0.
 __global__ __launch_bounds__(256) void flce_zero_kernel(float* __restrict__ dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
+}
+
+// Sum of the ksplit partial products of a split dH product, slice by slice
+// in order (so the result does not depend on scheduling). n4 = elements / 4.
+__global__ __launch_bounds__(256) void flce_ksum_kernel(const float* __restrict__ part, int S, int64_t n4,
+                                                        float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    f32x4 acc = ((const f32x4*)part)[i];
+    for (int s = 1; s < S; ++s) acc += ((const f32x4*)part)[(int64_t)s * n4 + i];
+    ((f32x4*)out)[i] = acc;
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -1087,8 +1108,22 @@ constexpr double kDzBudget = 2.0 * 1024 * 1024 * 1024;
 struct BwdPlan {
   int64_t N, D, V, Vp, Np, R, Rp;
   int dtype, chunks;
-  size_t es, off_wt, off_ht, off_dz, off_dzt, ws_bytes;
+  int ksplit, ks_per;  // bf16 dH: K slices and k-stages per slice
+  size_t es, off_wt, off_ht, off_dz, off_dzt, off_part, ws_bytes;
 };
+
+// K slices for the transposed-B dH product: when its tiles leave CUs idle,
+// split the contraction over V so that up to kSlots workgroups run, keeping
+// at least 16 k-stages (1024 of K) per slice and at most 16 slices.
+void gemmt_split(const Plan& ph, int* ksplit, int* ks_per) {
+  const int64_t grid = (int64_t)ph.row_blocks * ph.chunks;
+  const int ks_all = (ph.row_bytes + kStageRowBytes - 1) / kStageRowBytes;
+  int S = 1;
+  while (S < 16 && grid * (S + 1) <= kSlots && ks_all / (S + 1) >= 16) ++S;
+  const int per = (ks_all + S - 1) / S;
+  *ks_per = per;
+  *ksplit = (ks_all + per - 1) / per;
+}
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -1122,6 +1157,8 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
     bp->chunks = 0;
   }
   bp->Rp = round_up(bp->R, 8);
+  bp->ksplit = 1;
+  bp->ks_per = 0;
   // every pass must plan (32-bit offsets, resource sizes)
   Plan pl;
   int rc;
@@ -1129,6 +1166,7 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
     if ((rc = make_plan(bp->R, D, V, dtype, &pl)) != FLCE_OK) return rc;          // dZ
     if (dtype == FLCE_BF16) {
       if ((rc = make_plan(N, bp->Vp, D, dtype, &pl, kTile320)) != FLCE_OK) return rc;  // dH (transposed B)
+      gemmt_split(pl, &bp->ksplit, &bp->ks_per);
     } else {
       if ((rc = make_plan(D, bp->Vp, bp->R, dtype, &pl)) != FLCE_OK) return rc;   // dH
     }
@@ -1139,7 +1177,8 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
   bp->off_ht = align_up((size_t)(D * bp->Vp * es));
   bp->off_dz = bp->off_ht + align_up((size_t)(D * bp->Np * es));
   bp->off_dzt = bp->off_dz + (dtype == FLCE_BF16 ? 0 : align_up((size_t)(bp->Rp * bp->Vp * es)));
-  bp->ws_bytes = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Np * es));
+  bp->off_part = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Np * es));
+  bp->ws_bytes = bp->off_part + (bp->ksplit > 1 ? align_up((size_t)bp->ksplit * (size_t)(N * D) * 4) : 0);
   return FLCE_OK;
 }
 
@@ -1192,9 +1231,19 @@ int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32
     // dH[token][d] = sum_v dZ[token][v] W[v][d]: A = W^T [D][Vp], B = dZ read from dzt [Vp][Np]
     TileArgs g = tile_args(ph, dzt, wt);
     g.ldb = (int)bp.Np;
-    g.C = dH;
     g.ldc = (int)bp.D;
-    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, ph, g, stream);
+    g.ksplit = bp.ksplit;
+    g.ks_per = bp.ks_per;
+    float* part = (float*)(base + bp.off_part);
+    g.C = bp.ksplit > 1 ? part : dH;
+    Plan phs = ph;
+    phs.grid = ph.row_blocks * ph.chunks * bp.ksplit;
+    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, phs, g, stream);
+    if (bp.ksplit > 1) {
+      const int64_t n4 = bp.N * bp.D / 4;
+      hipLaunchKernelGGL(flce_ksum_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 2048)), dim3(256), 0,
+                         stream, (const float*)part, bp.ksplit, n4, dH);
+    }
   }
   for (int c = 0; c < (bf ? 0 : bp.chunks); ++c) {
     const int64_t r0 = (int64_t)c * bp.R;
@@ -1349,7 +1398,7 @@ int flce_backward(const void* H, const void* W, const int32_t* targets, const fl
   if (!W || !dW || !aligned(W, 16) || !aligned(dW, 4)) return FLCE_ERR_INVALID_ARG;
   if (N > 0) {
     if ((rc = check_inputs(H, W, targets, N)) != FLCE_OK) return rc;
-    if (!lse || !grad_loss || !dH || !aligned(lse, 4) || !aligned(grad_loss, 4) || !aligned(dH, 4))
+    if (!lse || !grad_loss || !dH || !aligned(lse, 4) || !aligned(grad_loss, 4) || !aligned(dH, 16))
       return FLCE_ERR_INVALID_ARG;
   }
   if (!workspace || workspace_bytes < bp.ws_bytes || !aligned(workspace, kAlign)) return FLCE_ERR_INVALID_ARG;

@@ -158,6 +158,7 @@ def test_backward_arguments_rejected_before_any_launch(flce):
         assert bwd(**{name: None}) == flce.FLCE_ERR_INVALID_ARG, name
     assert bwd(H=odd) == flce.FLCE_ERR_INVALID_ARG
     assert bwd(ws=odd) == flce.FLCE_ERR_INVALID_ARG
+    assert bwd(dH=odd) == flce.FLCE_ERR_INVALID_ARG        # dH takes 16-byte stores
     assert bwd(nb=need - 1) == flce.FLCE_ERR_INVALID_ARG
 
 
@@ -168,7 +169,9 @@ def test_backward_workspace_layout(flce):
     def up(x, m):
         return (x + m - 1) // m * m
 
+    splits = {}
     for N, D, V, dt, es in [(4, 8, 10, 0, 2), (128, 64, 1024, 1, 4), (8192, 4096, 151936, 0, 2),
+                            (2048, 1024, 32000, 0, 2), (4096, 2048, 50257, 0, 2),
                             (5000, 64, 262144, 0, 2), (0, 8, 10, 0, 2), (5000, 64, 262144, 1, 4),
                             (0, 8, 10, 1, 4)]:
         Vp, Np = up(V, 64), up(N, 64)
@@ -179,9 +182,17 @@ def test_backward_workspace_layout(flce):
             R = 0
         Rp = up(R, 8)
         want = (up(D * Vp * es, 256) + up(D * Np * es, 256) + up(Rp * Vp * es, 256) + up(Vp * Np * es, 256))
-        assert flce.flce_backward_workspace_bytes(N, D, V, dt) == want, (N, D, V, dt)
+        got = flce.flce_backward_workspace_bytes(N, D, V, dt)
+        # plus, where the bf16 dH product is split over the vocabulary, S partial N x D float32 sums
+        S = [s for s in range(1, 17) if got == want + (up(s * N * D * 4, 256) if s > 1 else 0)]
+        assert S, (N, D, V, dt, got, want)
+        assert S[0] == 1 or (dt == 0 and N > 0), (N, D, V, dt)
+        splits[(N, D, V, dt)] = S[0]
         if N and dt == 1:
             assert Rp * Vp * es <= 2 ** 31 + 256 * Vp * es    # one chunk of dZ stays near the budget
+    assert splits[(8192, 4096, 151936, 0)] == 1       # enough dH tiles to fill the chip alone
+    assert splits[(2048, 1024, 32000, 0)] > 1        # 32 dH tiles: split over the vocabulary
+    assert splits[(4, 8, 10, 0)] == 1                # too little K to split
     assert flce.flce_backward_workspace_bytes(4, 12, 10, 0) == 0   # unsupported D
 
 

@@ -123,6 +123,38 @@ def test_backward_production_shape_identities():
     _log(f"[bwd] prod identities: <dH,H>={ip_h:.6e} <dW,W>={ip_w:.6e}")
 
 
+@pytest.mark.parametrize("name", ["small_bf16", "medium_bf16"])
+def test_backward_vocabulary_split_workloads(name):
+    """The small and medium bf16 workloads, whose dH product has too few tiles
+    to fill the chip and is split over the vocabulary into partial sums (the
+    workspace is larger than W^T, H^T and dZ^T alone). Dense upstream gradient
+    1/N: sampled rows of dH against the oracle row by row; for the small
+    workload all of dW too; and the same bits on a second call."""
+    import linear_cross_entropy_amd as flce
+    w = workloads.WORKLOADS[name]
+    _log(f"[bwd] {w.describe()} vocabulary split")
+    up = lambda x: (x + 63) // 64 * 64
+    base = sum((n * 2 + 255) // 256 * 256 for n in (w.D * up(w.V), w.D * up(w.N), up(w.V) * up(w.N)))
+    assert flce.flce_backward_workspace_bytes(w.N, w.D, w.V, "bf16") > base
+    H, W, y = workloads.make(w, DEV)
+    g = torch.full((w.N,), 1.0 / w.N, dtype=torch.float32, device=DEV)
+    _, lse = flce.flce_forward(H, W, y)
+    dH, dW = flce.flce_backward(H, W, y, lse, g)
+    dH2, dW2 = flce.flce_backward(H, W, y, lse, g)
+    torch.cuda.synchronize()
+    assert torch.equal(dH, dH2) and torch.equal(dW, dW2), "second call differs"
+    rows = workloads.subset_rows(w.N, 24, seed=11).numpy()
+    full = name == "small_bf16"
+    ref = oracle.backward(H.cpu(), W.cpu(), y.cpu(), g.cpu(), rows=None if full else rows, want_dW=full)
+    ref_dH = ref["dH"][rows] if full else ref["dH"]
+    ref_abs = ref["dH_abs"][rows] if full else ref["dH_abs"]
+    check_bwd(dH[torch.as_tensor(rows, device=DEV)].cpu().numpy(), ref_dH, ref_abs, H.dtype, w.V,
+              f"{name} dH sampled rows")
+    if full:
+        e, rel = check_bwd(dW.cpu().numpy(), ref["dW"], ref["dW_abs"], H.dtype, w.N, f"{name} dW")
+        _log(f"[bwd] {name} dW max |d| {e:.3e}, relative Frobenius error {rel:.2e}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_backward_ragged_rows_and_row_chunks(dtype):
     """N=5000, V=262144 with the upstream gradient on a few rows (the others
