@@ -56,6 +56,15 @@ class Workload:
     def describe(self) -> str:
         return f"{self.name}: N={self.N} D={self.D} V={self.V} {self.dtype}"
 
+    def recipe(self) -> str:
+        """How the inputs are drawn, in words."""
+        cast = "rounded to bf16" if self.dtype == "bf16" else "kept fp32"
+        w = f"W ~ N(0,{self.w_std:g})"
+        if self.outlier_rows:
+            w += f" with {self.outlier_rows} seeded rows x{self.outlier_scale:g}"
+        y = "Zipf(1.1) int32 targets" if self.targets == "zipf" else "uniform int32 targets"
+        return f"synthetic (seeded; H ~ N(0,{self.h_std:g}), {w}, {cast}, {y})"
+
 
 WORKLOADS = {
     w.name: w
