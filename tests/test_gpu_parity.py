@@ -4,7 +4,8 @@ Every case runs the library through its C ABI (via the ctypes binding) and
 the oracle on the host. Large workloads compare a sampled subset of rows
 (first, last and seeded random rows) against the oracle and check the bound
 invariants max z <= lse <= max z + ln V (via loss >= 0 and finiteness) on
-every row.
+every row; every row of the large workloads is also compared with a plain
+PyTorch fp32 computation on the GPU.
 """
 import math
 
@@ -55,6 +56,41 @@ def test_workload_parity(name, sample):
     assert np.isfinite(loss).all() and np.isfinite(lse).all()
     assert (loss >= -2e-3).all(), "loss below 0 beyond rounding"
     _log(f"[parity] {name}: max |d| = {err:.3e}")
+
+
+@pytest.mark.parametrize("name", ["medium_bf16", "prod_bf16", "stress_bf16"])
+def test_every_row_against_torch_fp32(name):
+    """Every row at the full size against a plain PyTorch computation on the
+    GPU: the fp32 product of the bf16 inputs (exact products, fp32 sums), then
+    logsumexp and the target logit per row. It shares nothing with the
+    library or the oracle. The gate is the bf16 tolerance; both sides sum in
+    fp32 in different orders, so the 16 rows where they differ most also go
+    to the float64 oracle, which decides (at stress the outlier logits reach
+    a few hundred and the two differ by up to ~1e-3 there)."""
+    w = workloads.WORKLOADS[name]
+    _log(f"[torch] {w.describe()} all rows")
+    H, W, y = workloads.make(w, DEV)
+    loss, lse = gpu_forward(H, W, y)
+    Wt = W.float().t().contiguous()
+    ref_lse, ref_loss = [], []
+    for r0 in range(0, w.N, 1024):
+        Z = torch.mm(H[r0:r0 + 1024].float(), Wt)
+        l = torch.logsumexp(Z, dim=1)
+        ref_lse.append(l.cpu())
+        ref_loss.append((l - Z.gather(1, y[r0:r0 + 1024].long()[:, None])[:, 0]).cpu())
+        del Z
+    del Wt
+    t_lse = torch.cat(ref_lse).double().numpy()
+    t_loss = torch.cat(ref_loss).double().numpy()
+    e1 = check_close(lse, t_lse, H.dtype, f"{name} lse vs torch")
+    e2 = check_close(loss, t_loss, H.dtype, f"{name} loss vs torch")
+    worst = np.argsort(np.maximum(np.abs(lse - t_lse), np.abs(loss - t_loss)))[-16:]
+    rl, rs, _ = oracle.forward(H.cpu(), W.cpu(), y.cpu(), rows=worst)
+    e3 = check_close(lse[worst], rs, H.dtype, f"{name} lse on the rows torch disagrees most")
+    e4 = check_close(loss[worst], rl, H.dtype, f"{name} loss on the rows torch disagrees most")
+    et = max(np.abs(t_lse[worst] - rs).max(), np.abs(t_loss[worst] - rl).max())
+    _log(f"[torch] {name}: max |d| vs torch: lse {e1:.3e} loss {e2:.3e}; on those 16 rows vs the "
+         f"oracle: kernel {max(e3, e4):.3e}, torch {et:.3e}")
 
 
 # ------------------------------------------------------------------ edge grid
