@@ -30,7 +30,9 @@
 // and runs the two products dW = dZ^T H with a store epilogue
 // (flce_gemm_kernel) on K-contiguous transposed copies (flce_transpose_kernel)
 // and dH = dZ W, for bf16 reading dZ from its transposed copy through
-// transposing LDS reads (flce_gemmt_kernel).
+// transposing LDS reads (flce_gemmt_kernel); when that product's tiles would
+// leave compute units idle, its contraction over the vocabulary is split
+// into float32 partial sums that flce_ksum_kernel adds in a fixed order.
 
 #include <hip/hip_runtime.h>
 
@@ -109,7 +111,7 @@ typedef TileCfg<384, 256, 2, 4> Tile384;
 // along the tile's vocabulary axis, B: the rows along its token axis).
 enum TileMode {
   kForward = 0,  // online (max, sum) per token, target capture, per-chunk partials
-  kDz = 1,       // dZ = g (softmax - onehot), written row-major and transposed
+  kDz = 1,       // dZ = g (softmax - onehot), written transposed (and row-major if dz is set)
   kGemm = 2,     // plain C[a][b] = Z
   kGemmT = 3,    // C[b][a] = Z with B read from a [k][b] matrix (bf16 only)
 };
@@ -126,7 +128,8 @@ struct TileArgs {
   float* part_m;      // [chunks][N]
   float* part_s;      // [chunks][N]
   float* z_target;    // [N]
-  // kDz: lse and upstream gradient per token; dZ as [tok][dz_ld] and [v][dzt_ld]
+  // kDz: lse and upstream gradient per token; dZ as [v][dzt_ld] and, when dz is
+  // not null, also as [tok][dz_ld]
   const float* lse;
   const float* grad;
   char* dz;
