@@ -103,6 +103,25 @@ def test_edge_shapes(N, D, V, dt):
     parity(H, W, y, what=f"edge N={N} D={D} V={V} {dt}")
 
 
+@pytest.mark.parametrize("N,D,V,dt", [(5, 1 << 21, 1000, "bf16"), (3, 1 << 20, 300, "fp32")],
+                         ids=lambda v: str(v))
+def test_longest_rows_one_tile_per_chunk(N, D, V, dt):
+    """Rows of 4 MiB (D = 2^21 bf16, 2^20 fp32): one 256-row vocabulary tile
+    of W is then 1 GiB, so the planner's limit of 2^31 bytes per chunk (one
+    buffer resource) leaves one tile per chunk, and every tile runs 32768
+    k-stages. Against the oracle on every row."""
+    import linear_cross_entropy_amd as flce
+    plan = flce.flce_get_plan(N, D, V, dt)
+    assert plan["chunks"] == plan["vocab_tiles"] > 1, plan
+    assert plan["tile_vocab"] * D * (2 if dt == "bf16" else 4) < 2 ** 31
+    _log(f"[long] N={N} D={D} V={V} {dt} plan {plan}")
+    H, W, y = workloads.make_custom(N, D, V, dt, seed=23, device=DEV, h_std=1.0,
+                                    w_std=1.0 / math.sqrt(D))
+    y[0] = V - 1                      # a target in the last, ragged tile
+    _, _, err = parity(H, W, y, what=f"long rows N={N} D={D} V={V} {dt}")
+    _log(f"[long] max |d| = {err:.3e}")
+
+
 @pytest.mark.parametrize("N,D,V", BOUNDARY_SHAPES, ids=lambda v: str(v))
 def test_targets_on_tile_and_chunk_boundaries(N, D, V):
     """Targets at 0, V-1 and either side of every tile and chunk boundary."""
