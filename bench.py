@@ -153,7 +153,8 @@ def bench_backward(args, w):
         b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    each = [a.elapsed_time(b) for a, b in ev]
+    ms = sorted(each)
     avg = sum(ms) / len(ms)
     flops = 3 * w.flops
     peak = PEAK_TFLOPS[w.dtype]
@@ -186,6 +187,7 @@ def bench_backward(args, w):
             "kernel_ms_avg": avg,
             "kernel_ms_median": ms[len(ms) // 2],
             "kernel_ms_min": ms[0],
+            "kernel_ms_each": [round(t, 4) for t in each],
         },
         "outputs_finite": bool(torch.isfinite(dH).all().item() and torch.isfinite(dW).all().item()),
     }
@@ -308,6 +310,7 @@ def main():
             "kernel_ms_avg": avg_ms,
             "kernel_ms_median": kernel_ms_sorted[len(kernel_ms) // 2],
             "kernel_ms_min": kernel_ms_sorted[0],
+            "kernel_ms_each": [round(t, 4) for t in kernel_ms],
         },
         "outputs_finite": sanity,
         "kernel_source_sha": kernel_source_sha(),
