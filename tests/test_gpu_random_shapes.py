@@ -1,0 +1,77 @@
+"""Seeded random shapes: forward and backward against the oracle on every row.
+
+The fixed grids in parity.py are chosen by hand for known edges; these shapes
+are drawn once from a fixed seed over wide ranges (N from 1 to 6000,
+D any multiple of 8 (bf16) or 4 (fp32) up to 2048, V from 1 to 150000), so they
+reach tile choices, chunk counts, ragged tails and vocabulary-split factors of
+the backward that no hand-written case names. Each case is sized so that the
+oracle finishes in about a second.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import parity, parity_backward
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _shapes(seed, count, budget):
+    """count (N, D, V, dtype) with N*D*V <= budget: every other one drawn
+    log-uniformly over the whole ranges, the others with N >= 512 and
+    V >= 4000 (the sizes where the planner picks larger tiles and several
+    chunks) and D log-uniform up to what the budget leaves."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        dt = "bf16" if rng.random() < 0.8 else "fp32"
+        step = 8 if dt == "bf16" else 4
+        if len(out) % 2 == 0:
+            N = int(np.exp(rng.uniform(0, np.log(6000))))
+            V = int(np.exp(rng.uniform(0, np.log(150000))))
+            dmax = 2048
+        else:
+            N = int(np.exp(rng.uniform(np.log(512), np.log(6000))))
+            V = int(np.exp(rng.uniform(np.log(4000), np.log(150000))))
+            dmax = min(2048, int(budget // (N * V)))
+        if dmax < step:
+            continue
+        D = step * int(np.exp(rng.uniform(0, np.log(dmax // step))))
+        if N * D * V <= budget:
+            out.append((N, D, V, dt))
+    return out
+
+
+FWD_SHAPES = _shapes(2024, 24, 1.5e10)
+BWD_SHAPES = _shapes(4048, 12, 1.5e9)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _inputs(N, D, V, dt, seed):
+    std = 1.0 if dt == "bf16" else 0.5
+    return workloads.make_custom(N, D, V, dt, seed=seed, device=DEV, h_std=std,
+                                 w_std=2.0 / np.sqrt(D))
+
+
+@pytest.mark.parametrize("N,D,V,dt", FWD_SHAPES, ids=lambda v: str(v))
+def test_random_shape_forward(N, D, V, dt):
+    print(f"[random fwd] N={N} D={D} V={V} {dt}", flush=True)
+    H, W, y = _inputs(N, D, V, dt, seed=N + 3 * D + 7 * V)
+    parity(H, W, y, what=f"random fwd N={N} D={D} V={V} {dt}")
+
+
+@pytest.mark.parametrize("N,D,V,dt", BWD_SHAPES, ids=lambda v: str(v))
+def test_random_shape_backward(N, D, V, dt):
+    print(f"[random bwd] N={N} D={D} V={V} {dt}", flush=True)
+    H, W, y = _inputs(N, D, V, dt, seed=5 * N + D + 11 * V)
+    g = torch.linspace(0.25, 1.75, N, dtype=torch.float32).to(DEV)
+    parity_backward(H, W, y, g, what=f"random bwd N={N} D={D} V={V} {dt}")
