@@ -35,6 +35,10 @@
  *     no abort); on an error status nothing has been enqueued.
  *   - All entry points are thread-safe and reentrant. Concurrent calls may
  *     share H and W but not outputs or a workspace.
+ *   - Every entry point except flce_forward enqueues kernel launches only (no
+ *     allocation, no memset, no copy), so it can be captured into a HIP graph
+ *     and replayed; flce_forward adds a stream-ordered allocation and free of
+ *     its workspace.
  *   - Accumulation is fp32 (bf16 x bf16 and fp32 x fp32 products on the
  *     matrix cores); outputs are fp32.
  */
