@@ -797,27 +797,33 @@ __global__ __launch_bounds__(C::THREADS, 1) void flce_gemmt_kernel(TileArgs p) {
   tile_loop<T, C, kGemmT>(p);
 }
 
-// Merge: one thread per token, in double precision (a handful of operations
-// per row). With off(m) = fl(m log2 e) as in the partials kernel,
-// C = max_c off(m_c), S = sum_c s_c 2^(off(m_c) - C), lse = (C + log2 S) ln 2
-// and loss = lse - z_y (NaN when y is not in [0, V)).
-__global__ __launch_bounds__(256) void flce_merge_kernel(const float* __restrict__ part_m,
-                                                         const float* __restrict__ part_s,
-                                                         const float* __restrict__ z_target,
-                                                         const int32_t* __restrict__ y, int N, int V,
-                                                         int chunks, float* __restrict__ loss,
-                                                         float* __restrict__ lse) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+// Merge: one thread per token. With off(m) = fl(m log2 e) as in the partials
+// kernel, C = max_c off(m_c), S = sum_c s_c 2^(off(m_c) - C),
+// lse = (C + log2 S) ln 2 and loss = lse - z_y (NaN when y is not in [0, V)).
+// C is a maximum of fp32 values (exact); each weight 2^(off(m_c) - C) is the
+// hardware fp32 exp2 of the difference (relative error ~1e-6 for every weight
+// above 2^-30, far below the partial sums' own rounding); S and the final
+// logarithm are carried in double. A NaN in m or s reaches S and the row's
+// lse and loss.
+constexpr int kMergeThreads = 64;
+__global__ __launch_bounds__(kMergeThreads) void flce_merge_kernel(const float* __restrict__ part_m,
+                                                                   const float* __restrict__ part_s,
+                                                                   const float* __restrict__ z_target,
+                                                                   const int32_t* __restrict__ y, int N, int V,
+                                                                   int chunks, float* __restrict__ loss,
+                                                                   float* __restrict__ lse) {
+  const int i = blockIdx.x * kMergeThreads + threadIdx.x;
   if (i >= N) return;
-  double C = -__builtin_inf();
-  for (int c = 0; c < chunks; ++c) C = fmax(C, (double)off2(part_m[(size_t)c * N + i]));
+  float C = kNegInf;
+  for (int c = 0; c < chunks; ++c) C = fmaxf(C, off2(part_m[(size_t)c * N + i]));
   double S = 0.0;
+#pragma unroll 4
   for (int c = 0; c < chunks; ++c) {
-    const double o = (double)off2(part_m[(size_t)c * N + i]);
-    const double w = (o == -__builtin_inf()) ? 0.0 : exp2(o - C);
-    S += (double)part_s[(size_t)c * N + i] * w;
+    const float o = off2(part_m[(size_t)c * N + i]);
+    const float w = (o == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(o - C);
+    S += (double)part_s[(size_t)c * N + i] * (double)w;
   }
-  const double l = (C + log2(S)) * 0.69314718055994530942;
+  const double l = ((double)C + log2(S)) * 0.69314718055994530942;
   if (lse) lse[i] = (float)l;
   const int t = y[i];
   loss[i] = (t >= 0 && t < V) ? (float)(l - (double)z_target[i]) : __builtin_nanf("");
@@ -1086,7 +1092,8 @@ int launch_merge(const Plan& pl, const int32_t* y, float* loss, float* lse, cons
   const float* m = (const float*)((const char*)ws + pl.off_m);
   const float* s = (const float*)((const char*)ws + pl.off_s);
   const float* z = (const float*)((const char*)ws + pl.off_z);
-  hipLaunchKernelGGL(flce_merge_kernel, dim3((pl.N + 255) / 256), dim3(256), 0, stream, m, s, z, y,
+  hipLaunchKernelGGL(flce_merge_kernel, dim3((pl.N + kMergeThreads - 1) / kMergeThreads), dim3(kMergeThreads), 0,
+                     stream, m, s, z, y,
                      pl.N, pl.V, pl.chunks, loss, lse);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
