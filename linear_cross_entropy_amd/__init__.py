@@ -15,6 +15,7 @@ device memory and the stream. The functions keep the C names:
     flce_backward_workspace_bytes(N, D, V, dtype) -> int
     flce_status_string(status) -> str
     flce_version() -> int
+    linear_cross_entropy(H, W, targets) -> loss   (torch.autograd: gradients for H and W)
 
 The operation (page "Een gefuseerde forward-kernel
 voor lineaire cross-entropy op Apple-GPU's", section 1): with logits Z = H W^T, lse_i = logsumexp(Z_i) and
@@ -268,3 +269,33 @@ def flce_backward(H, W, targets, lse, grad_loss, workspace=None, dH=None, dW=Non
 def forward(H, W, targets):
     """Convenience: (loss, lse) on the current stream with a library-managed workspace."""
     return flce_forward(H, W, targets)
+
+
+class LinearCrossEntropy(torch.autograd.Function):
+    """Per-token loss with gradients for H and W: the forward runs flce_forward
+    and keeps its lse; the backward hands the incoming per-token gradient to
+    flce_backward, which regenerates the logits tile by tile (the page's
+    training path: the forward's log-sum-exp is kept, the logits are not).
+    The float32 gradients are cast to the inputs' dtype by autograd itself."""
+
+    @staticmethod
+    def forward(ctx, H, W, targets):
+        loss, lse = flce_forward(H, W, targets)
+        ctx.save_for_backward(H, W, targets, lse)
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        H, W, targets, lse = ctx.saved_tensors
+        if not (ctx.needs_input_grad[0] or ctx.needs_input_grad[1]):
+            return None, None, None
+        g = grad_loss.to(torch.float32).contiguous()
+        dH, dW = flce_backward(H, W, targets, lse, g)
+        return (dH if ctx.needs_input_grad[0] else None,
+                dW if ctx.needs_input_grad[1] else None, None)
+
+
+def linear_cross_entropy(H, W, targets):
+    """loss_i = logsumexp(H_i W^T) - (H_i W^T)[y_i] per token (float32, shape
+    (N,)), differentiable in H and W; reduce it (mean, weights) as needed."""
+    return LinearCrossEntropy.apply(H, W, targets)
