@@ -297,5 +297,9 @@ class LinearCrossEntropy(torch.autograd.Function):
 
 def linear_cross_entropy(H, W, targets):
     """loss_i = logsumexp(H_i W^T) - (H_i W^T)[y_i] per token (float32, shape
-    (N,)), differentiable in H and W; reduce it (mean, weights) as needed."""
+    (N,)), differentiable in H and W; reduce it (mean, weights) as needed.
+    A target outside [0, V) (an ignored position) gives that row a NaN loss:
+    select the valid rows before reducing, e.g. loss[y >= 0].mean(); the
+    ignored rows then receive a zero upstream gradient and contribute nothing
+    to dH or dW."""
     return LinearCrossEntropy.apply(H, W, targets)

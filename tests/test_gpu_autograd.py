@@ -74,3 +74,27 @@ def test_autograd_only_the_inputs_that_need_it():
     torch.cuda.synchronize()
     assert W0.grad is None
     assert torch.equal(H.grad, dH.to(H0.dtype))
+
+
+def test_autograd_ignored_positions():
+    """Targets of -100 on some rows: their loss is NaN, and reducing over the
+    valid rows gives the gradients of those rows alone (the oracle on the
+    valid sub-batch for dW; zero dH on the ignored rows)."""
+    import linear_cross_entropy_amd as flce
+    N, D, V = 300, 128, 4001
+    H0, W0, y = workloads.make_custom(N, D, V, "fp32", seed=67, device=DEV, h_std=0.5,
+                                      w_std=1.0 / np.sqrt(D))
+    y = y.clone()
+    y[::7] = -100
+    H = H0.clone().requires_grad_(True)
+    W = W0.clone().requires_grad_(True)
+    loss = flce.linear_cross_entropy(H, W, y)
+    valid = y >= 0
+    assert bool(torch.isnan(loss[~valid]).all()) and bool(torch.isfinite(loss[valid]).all())
+    loss[valid].sum().backward()
+    torch.cuda.synchronize()
+    assert bool((H.grad[~valid] == 0).all())
+    sel = valid.cpu()
+    ref = oracle.backward(H0.cpu()[sel], W0.cpu(), y.cpu()[sel], torch.ones(int(sel.sum()), dtype=torch.float32))
+    check_bwd(H.grad.cpu().numpy()[sel.numpy()], ref["dH"], ref["dH_abs"], H0.dtype, V, "ignored rows: dH")
+    check_bwd(W.grad.cpu().numpy(), ref["dW"], ref["dW_abs"], H0.dtype, N, "ignored rows: dW")
