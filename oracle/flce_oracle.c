@@ -1,7 +1,7 @@
 /*
  * Oracle for the linear cross-entropy forward and its backward.
  * TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
- * CPU-baseline leg use it to judge the GPU library; the library never calls
+ * CPU-baseline leg use it to check the GPU library; the library never calls
  * it.
  *
  * It is the plain definition from "Een gefuseerde forward-kernel
