@@ -199,6 +199,80 @@ def bench_backward(args, w):
     print(json.dumps(result), flush=True)
 
 
+def bench_quant(args, w):
+    """The forward with a quantised head of the workload's shape: each step is
+    one flce_forward_quant (dequantisation slice by slice, the partials kernel
+    per slice, one merge), timed whole with HIP events on the launch stream."""
+    import torch
+    import linear_cross_entropy_amd as flce
+    import workloads
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.describe()} with a {args.quant}-bit head, group {args.group}",
+          file=sys.stderr, flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(w.N, w.D, w.V, args.quant, args.group, seed=w.index,
+                                                       device=dev)
+    ws = torch.empty(flce.flce_forward_quant_workspace_bytes(w.N, w.D, w.V, args.quant, args.group),
+                     dtype=torch.uint8, device=dev)
+    loss = torch.empty(w.N, device=dev)
+    lse = torch.empty(w.N, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        flce.flce_forward_quant(H, codes, scales, biases, y, args.quant, args.group, workspace=ws,
+                                loss=loss, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    each = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(each) / len(each)
+    achieved = w.flops / (avg * 1e-3) / 1e12
+    head_bytes = codes.numel() + 2 * scales.numel() * 4
+    result = {
+        "metric": f"tokens/s + % bf16 MFMA peak, fused LCE fwd with a {args.quant}-bit head "
+                  f"N={w.N} D={w.D} V={w.V}",
+        "value": w.N * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": f"synthetic (seeded; H ~ N(0,1) bf16, uniform {args.quant}-bit codes, per-group scales and "
+                f"biases for weights of spread ~0.02, uniform int32 targets)",
+        "config": {"workload": w.name, "N": w.N, "D": w.D, "V": w.V, "bits": args.quant, "group": args.group,
+                   "head_bytes": head_bytes, "workspace_bytes": ws.numel()},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "flce_forward_quant (all launches: dequantisation per slice, partials per slice, merge)",
+            "achieved": achieved,
+            "peak": PEAK_TFLOPS["bf16"],
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_TFLOPS["bf16"],
+            "traffic": None,
+            "algorithmic_flop_per_launch": w.flops,
+            "kernel_ms_avg": avg,
+            "kernel_ms_median": sorted(each)[len(each) // 2],
+            "kernel_ms_min": min(each),
+            "kernel_ms_each": [round(t, 4) for t in each],
+        },
+        "outputs_finite": bool(torch.isfinite(loss).all().item()),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +287,9 @@ def main():
                     help="only run a plain copy of BYTES bytes (counter scaling), then exit")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (flce_backward, given the forward's lse) instead of the forward")
+    ap.add_argument("--quant", type=int, default=0, choices=(0, 4, 8), metavar="BITS",
+                    help="time flce_forward_quant with a BITS-bit head of the workload's shape instead")
+    ap.add_argument("--group", type=int, default=64, help="weights per scale/bias group with --quant")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -235,6 +312,9 @@ def main():
     w = workloads.WORKLOADS[args.workload]
     if args.backward:
         bench_backward(args, w)
+        return
+    if args.quant:
+        bench_quant(args, w)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)

@@ -164,6 +164,44 @@ int flce_backward(const void* H, const void* W, const int32_t* targets,
  * unsupported shape). */
 size_t flce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype);
 
+/*
+ * Forward with a quantised output head. The page mentions output heads stored
+ * quantised (section 2: its first, chunked prototype handled dense and
+ * quantised heads; section 9 leaves the quantised variants of the fused kernel
+ * out of scope) but fixes no format. This library takes a groupwise affine
+ * one: W (V x D) is given as unsigned integer codes q with one float32 scale
+ * and one float32 bias per group of `group` consecutive weights of a row, and
+ * the head the forward uses is, weight by weight,
+ *
+ *     w[v][d] = bf16( fl32( fl32(scale[v][g] * q[v][d]) + bias[v][g] ) ),
+ *     g = d / group,  bf16() rounding to nearest even,
+ *
+ * after which loss and lse are exactly as flce_forward computes them for H
+ * and that bf16 W.
+ *   - H is bf16, N x D as for flce_forward (16-byte aligned, D % 8 == 0).
+ *   - bits is 8 (codes: V x D bytes, row-major) or 4 (V x D/2 bytes: byte b
+ *     of a row holds weight 2b in its low nibble and 2b+1 in its high one);
+ *     codes 16-byte aligned.
+ *   - group: a multiple of 8 that divides D; scales and biases are float32
+ *     [V][D / group], 4-byte aligned.
+ *   - The vocabulary is dequantised slice by slice (about 256 MB of bf16 at a
+ *     time) into the workspace, so device memory stays at the codes plus one
+ *     slice; a vocabulary that fits one slice gives the same bits as
+ *     flce_forward on the dequantised W.
+ *   - workspace: flce_forward_quant_workspace_bytes(N, D, V, bits, group)
+ *     bytes, 256-byte aligned (FLCE_ERR_INVALID_ARG if smaller). Allocates
+ *     nothing. bits not 4 or 8, or a bad group: FLCE_ERR_UNSUPPORTED. Other
+ *     conventions as for flce_forward.
+ */
+int flce_forward_quant(const void* H, const uint8_t* codes, const float* scales, const float* biases,
+                       const int32_t* targets, int64_t N, int64_t D, int64_t V, int bits, int group,
+                       float* loss_out, float* lse_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes flce_forward_quant needs (0 for N == 0 or an invalid or
+ * unsupported shape). */
+size_t flce_forward_quant_workspace_bytes(int64_t N, int64_t D, int64_t V, int bits, int group);
+
 /* Tile plan for a shape; FLCE_ERR_INVALID_ARG/UNSUPPORTED as flce_forward. */
 int flce_get_plan(int64_t N, int64_t D, int64_t V, int dtype, flce_plan_t* plan);
 

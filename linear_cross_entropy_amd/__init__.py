@@ -16,6 +16,8 @@ device memory and the stream. The functions keep the C names:
     flce_status_string(status) -> str
     flce_version() -> int
     linear_cross_entropy(H, W, targets) -> loss   (torch.autograd: gradients for H and W)
+    flce_forward_quant(H, codes, scales, biases, targets, bits, group, workspace=None, loss=None, lse=None, stream=None)
+    flce_forward_quant_workspace_bytes(N, D, V, bits, group) -> int
 
 The operation (page "Een gefuseerde forward-kernel
 voor lineaire cross-entropy op Apple-GPU's", section 1): with logits Z = H W^T, lse_i = logsumexp(Z_i) and
@@ -65,6 +67,10 @@ _lib.flce_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, 
 _lib.flce_backward.restype = _i32
 _lib.flce_backward_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32]
 _lib.flce_backward_workspace_bytes.restype = _sz
+_lib.flce_forward_quant.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _sz, _vp]
+_lib.flce_forward_quant.restype = _i32
+_lib.flce_forward_quant_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
+_lib.flce_forward_quant_workspace_bytes.restype = _sz
 _lib.flce_status_string.argtypes = [_i32]
 _lib.flce_status_string.restype = ctypes.c_char_p
 _lib.flce_version.argtypes = []
@@ -87,7 +93,8 @@ _lib.flce_get_plan.restype = _i32
 
 EXPORTED = ["flce_forward", "flce_forward_ws", "flce_partials", "flce_merge",
             "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version",
-            "flce_backward", "flce_backward_workspace_bytes"]
+            "flce_backward", "flce_backward_workspace_bytes",
+            "flce_forward_quant", "flce_forward_quant_workspace_bytes"]
 
 
 class FlceError(RuntimeError):
@@ -269,6 +276,48 @@ def flce_backward(H, W, targets, lse, grad_loss, workspace=None, dH=None, dW=Non
 def forward(H, W, targets):
     """Convenience: (loss, lse) on the current stream with a library-managed workspace."""
     return flce_forward(H, W, targets)
+
+
+def flce_forward_quant_workspace_bytes(N: int, D: int, V: int, bits: int, group: int) -> int:
+    return int(_lib.flce_forward_quant_workspace_bytes(N, D, V, bits, group))
+
+
+def flce_forward_quant(H, codes, scales, biases, targets, bits: int, group: int, workspace=None,
+                       loss=None, lse=None, stream=None):
+    """(loss, lse) for a quantised head: codes (V, D) uint8 at 8 bits or (V, D/2)
+    at 4 bits (two per byte, low nibble first), scales and biases float32
+    (V, D/group); see flce_forward_quant in include/flce.h for the format."""
+    for name, t in (("H", H), ("codes", codes), ("scales", scales), ("biases", biases), ("targets", targets)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous torch.Tensor on a GPU device")
+    if H.dtype != torch.bfloat16 or H.dim() != 2:
+        raise ValueError("H must be a (N, D) bfloat16 tensor")
+    N, D = H.shape
+    V = codes.shape[0]
+    if codes.dtype != torch.uint8 or codes.dim() != 2 or bits not in (4, 8) or \
+            codes.shape[1] != (D if bits == 8 else D // 2):
+        raise ValueError(f"codes must be uint8 of shape (V, {D if bits == 8 else D // 2}) for bits={bits}")
+    if group <= 0 or D % group:
+        raise ValueError(f"group must divide D={D}")
+    for name, t in (("scales", scales), ("biases", biases)):
+        if t.dtype != torch.float32 or t.shape != (V, D // group):
+            raise ValueError(f"{name} must be float32 of shape ({V}, {D // group})")
+    if targets.dtype != torch.int32 or targets.shape != (N,):
+        raise ValueError("targets must be int32 of shape (N,)")
+    dev = H.device
+    loss = _out(loss, N, dev, "loss")
+    lse = _out(lse, N, dev, "lse")
+    nbytes = flce_forward_quant_workspace_bytes(N, D, V, bits, group)
+    if N and nbytes == 0:
+        raise FlceError(FLCE_ERR_UNSUPPORTED, "flce_forward_quant_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = _lib.flce_forward_quant(_ptr(H), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(targets), N, D, V,
+                                 bits, group, _ptr(loss), _ptr(lse), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward_quant")
+    return loss, lse
 
 
 class LinearCrossEntropy(torch.autograd.Function):

@@ -33,6 +33,12 @@
 // transposing LDS reads (flce_gemmt_kernel); when that product's tiles would
 // leave compute units idle, its contraction over the vocabulary is split
 // into float32 partial sums that flce_ksum_kernel adds in a fixed order.
+//
+// Quantised head (the page's first prototype handled quantised output heads,
+// section 2; the format here is a reading, stated in flce.h): the vocabulary
+// runs in slices, each dequantised to bf16 by flce_dequant_kernel into the
+// workspace and run through the unchanged partials kernel with its targets
+// offset by the slice's first row; one merge covers all slices' chunks.
 
 #include <hip/hip_runtime.h>
 
@@ -124,6 +130,7 @@ struct TileArgs {
   int xcd_rows, xcd_chunks;  // XCD group shape; xcd_rows == 0 disables the remap
   // kForward and kDz
   const int32_t* y;   // [N] targets
+  int v_off;          // vocabulary index of W's first row: a target y counts as row y - v_off
   // kForward
   float* part_m;      // [chunks][N]
   float* part_s;      // [chunks][N]
@@ -418,7 +425,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     l2tok[nb] = 0.f;
     gtok[nb] = 0.f;
     if constexpr (MODE != kGemm) {
-      if (tok < p.N) ytok[nb] = p.y[tok];
+      if (tok < p.N) ytok[nb] = p.y[tok] - p.v_off;
     }
     if constexpr (MODE == kDz) {
       if (tok < p.N) {
@@ -886,6 +893,50 @@ __global__ __launch_bounds__(256) void flce_ksum_kernel(const float* __restrict_
   }
 }
 
+// Quantised output head: rows [0, rows) of the codes, dequantised to bf16.
+// Each thread turns 8 consecutive weights of a row (8 code bytes at 8 bits; 4
+// bytes at 4 bits, byte k holding weight 2k in its low nibble and 2k + 1 in
+// its high one) into 16 bytes of bf16, w = bf16(fl(fl(scale * q) + bias)) with
+// the scale and bias of the weights' group (group % 8 == 0, so the 8 share
+// one). Consecutive lanes write consecutive 16 bytes, so the stores, which
+// are most of the traffic, coalesce; giving a thread 16 or 32 weights (wider
+// code loads) broke that and was slower.
+template <int BITS>
+__global__ __launch_bounds__(256) void flce_dequant_kernel(const uint8_t* __restrict__ codes,
+                                                           const float* __restrict__ scales,
+                                                           const float* __restrict__ biases, int64_t rows,
+                                                           int D, int group, __bf16* __restrict__ out) {
+  const int per_row = D / 8;
+  const int groups = D / group;
+  const int64_t n = rows * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / per_row;
+    const int d0 = (int)(i - r * per_row) * 8;
+    const int64_t gi = r * groups + d0 / group;
+    const float sc = scales[gi], bi = biases[gi];
+    uint32_t q[8];
+    if constexpr (BITS == 8) {
+      const uint2 v = *(const uint2*)(codes + r * D + d0);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        q[k] = (v.x >> (8 * k)) & 0xFFu;
+        q[k + 4] = (v.y >> (8 * k)) & 0xFFu;
+      }
+    } else {
+      const uint32_t v = *(const uint32_t*)(codes + r * (D / 2) + d0 / 2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) q[k] = (v >> (4 * k)) & 0xFu;
+    }
+    bf16x8 w;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float prod = (float)q[k] * sc;
+      w[k] = (__bf16)(prod + bi);
+    }
+    *(bf16x8*)(out + r * D + d0) = w;
+  }
+}
+
 // ------------------------------------------------------------------ host side
 constexpr int kSlots = 256;       // workgroups resident at once: one per CU
 constexpr size_t kAlign = 256;
@@ -1291,6 +1342,92 @@ int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+// ------------------------------------------------------------------ quantised head
+// The vocabulary runs in slices of Vs rows: each slice is dequantised into a
+// bf16 buffer in the workspace and run through the partials kernel with its
+// chunks' partial states written after the previous slices' (and targets
+// offset by the slice's first row), then one merge covers every chunk. Vs is
+// a multiple of 3072 rows (8 chunks of 384-row tiles) with the buffer near
+// kQuantSliceBytes; a vocabulary that fits one slice is a single pass.
+constexpr double kQuantSliceBytes = 256.0 * 1024 * 1024;
+
+struct QuantPlan {
+  int64_t N, D, V, Vs;
+  int bits, group, slices, chunks_total;
+  Plan full, last;  // plans of a full slice and of the last one
+  size_t off_buf, off_m, off_s, off_z, ws_bytes;
+};
+
+int make_quant_plan(int64_t N, int64_t D, int64_t V, int bits, int group, QuantPlan* qp) {
+  if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
+  if ((bits != 4 && bits != 8) || group < 8 || group % 8 != 0 || D % group != 0) return FLCE_ERR_UNSUPPORTED;
+  qp->N = N;
+  qp->D = D;
+  qp->V = V;
+  qp->bits = bits;
+  qp->group = group;
+  int64_t vs = (int64_t)(kQuantSliceBytes / (double)(D * 2)) / 3072 * 3072;
+  if (vs < 3072) vs = 3072;
+  qp->Vs = std::min(vs, V);
+  qp->slices = (int)((V + qp->Vs - 1) / qp->Vs);
+  int rc;
+  if ((rc = make_plan(N, D, qp->Vs, FLCE_BF16, &qp->full)) != FLCE_OK) return rc;
+  const int64_t v_last = V - (int64_t)(qp->slices - 1) * qp->Vs;
+  if ((rc = make_plan(N, D, v_last, FLCE_BF16, &qp->last)) != FLCE_OK) return rc;
+  if (V > INT32_MAX / 2) return FLCE_ERR_UNSUPPORTED;
+  const int64_t C = (int64_t)(qp->slices - 1) * qp->full.chunks + qp->last.chunks;
+  if (C > INT32_MAX) return FLCE_ERR_UNSUPPORTED;
+  qp->chunks_total = (int)C;
+  qp->off_buf = 0;
+  qp->off_m = align_up((size_t)(qp->Vs * D * 2));
+  qp->off_s = qp->off_m + align_up((size_t)C * N * sizeof(float));
+  qp->off_z = qp->off_s + align_up((size_t)C * N * sizeof(float));
+  qp->ws_bytes = qp->off_z + align_up((size_t)N * sizeof(float));
+  return FLCE_OK;
+}
+
+void launch_dequant(int bits, int D, int group, const uint8_t* codes, const float* scales, const float* biases,
+                    int64_t rows, __bf16* out, hipStream_t stream) {
+  const int64_t n = rows * (D / 8);
+  const dim3 grid((unsigned)std::min<int64_t>((n + 255) / 256, 8192)), block(256);
+  if (bits == 8)
+    hipLaunchKernelGGL((flce_dequant_kernel<8>), grid, block, 0, stream, codes, scales, biases, rows, D, group, out);
+  else
+    hipLaunchKernelGGL((flce_dequant_kernel<4>), grid, block, 0, stream, codes, scales, biases, rows, D, group, out);
+}
+
+int launch_forward_quant(const QuantPlan& qp, const void* H, const uint8_t* codes, const float* scales,
+                         const float* biases, const int32_t* y, float* loss, float* lse, void* ws,
+                         hipStream_t stream) {
+  char* base = (char*)ws;
+  __bf16* buf = (__bf16*)(base + qp.off_buf);
+  float* m = (float*)(base + qp.off_m);
+  float* s = (float*)(base + qp.off_s);
+  float* z = (float*)(base + qp.off_z);
+  const size_t code_row = (size_t)(qp.bits == 8 ? qp.D : qp.D / 2);
+  const int64_t groups = qp.D / qp.group;
+  int64_t c0 = 0;
+  for (int k = 0; k < qp.slices; ++k) {
+    const Plan& pl = k + 1 < qp.slices ? qp.full : qp.last;
+    const int64_t v0 = (int64_t)k * qp.Vs;
+    const int64_t rows = pl.V;
+    launch_dequant(qp.bits, (int)qp.D, qp.group, codes + v0 * code_row, scales + v0 * groups, biases + v0 * groups,
+                   rows, buf, stream);
+    TileArgs a = tile_args(pl, H, buf);
+    a.y = y;
+    a.v_off = (int)v0;
+    a.part_m = m + c0 * qp.N;
+    a.part_s = s + c0 * qp.N;
+    a.z_target = z;
+    FLCE_LAUNCH_TILES(flce_partials_kernel, pl, a, stream);
+    c0 += pl.chunks;
+  }
+  hipLaunchKernelGGL(flce_merge_kernel, dim3((unsigned)((qp.N + kMergeThreads - 1) / kMergeThreads)),
+                     dim3(kMergeThreads), 0, stream, (const float*)m, (const float*)s, (const float*)z, y,
+                     (int)qp.N, (int)qp.V, qp.chunks_total, loss, lse);
+  return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1413,6 +1550,28 @@ int flce_backward(const void* H, const void* W, const int32_t* targets, const fl
   }
   if (!workspace || workspace_bytes < bp.ws_bytes || !aligned(workspace, kAlign)) return FLCE_ERR_INVALID_ARG;
   return launch_backward(bp, H, W, targets, lse, grad_loss, dH, dW, workspace, (hipStream_t)stream);
+}
+
+size_t flce_forward_quant_workspace_bytes(int64_t N, int64_t D, int64_t V, int bits, int group) {
+  QuantPlan qp;
+  if (N == 0 || make_quant_plan(N, D, V, bits, group, &qp) != FLCE_OK) return 0;
+  return qp.ws_bytes;
+}
+
+int flce_forward_quant(const void* H, const uint8_t* codes, const float* scales, const float* biases,
+                       const int32_t* targets, int64_t N, int64_t D, int64_t V, int bits, int group,
+                       float* loss_out, float* lse_out, void* workspace, size_t workspace_bytes, void* stream) {
+  QuantPlan qp;
+  int rc = make_quant_plan(N, D, V, bits, group, &qp);
+  if (rc != FLCE_OK) return rc;
+  if (N == 0) return FLCE_OK;
+  if (!H || !codes || !scales || !biases || !targets || !loss_out) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(H, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(biases, 4) ||
+      !aligned(targets, 4) || !aligned(loss_out, 4) || (lse_out && !aligned(lse_out, 4)))
+    return FLCE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < qp.ws_bytes || !aligned(workspace, kAlign)) return FLCE_ERR_INVALID_ARG;
+  return launch_forward_quant(qp, H, codes, scales, biases, targets, loss_out, lse_out, workspace,
+                              (hipStream_t)stream);
 }
 
 }  // extern "C"

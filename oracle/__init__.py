@@ -11,6 +11,13 @@ marshals arguments. It shares no code with the GPU library.
 
 Pins (what ties it to something other than itself) are the ``not gpu`` tests
 in ``tests/test_oracle_pins.py`` and ``tests/test_oracle_mutants.py``.
+
+``dequantize`` writes out the quantised-head format the library takes for
+the page's quantised output heads (section 2 mentions them; no format is
+fixed there, so the format is a reading, stated with the library's
+flce_forward_quant): it is pinned by closed forms in
+``tests/test_oracle_quant.py``, while the choice of format itself has
+nothing on the page to be checked against (parity unpinned in that sense).
 """
 from __future__ import annotations
 
@@ -184,4 +191,43 @@ def backward(H, W, y, g, rows=None, want_dW=True, lib=None):
         out["dW"] = dW
         out["dW_abs"] = dW_abs
     return out
+
+
+def _bf16_rne_bits(x32: np.ndarray) -> np.ndarray:
+    """float32 array -> bfloat16 bit patterns (uint16), rounding to nearest,
+    ties to even (inputs here are finite)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def dequantize(codes, scales, biases, bits: int, group: int) -> np.ndarray:
+    """bf16 bit patterns (uint16, V x D) of the quantised head
+    w[v][d] = bf16(fl32(fl32(scale[v][d // group] * q[v][d]) + bias[v][d // group])).
+
+    codes: uint8, V x D (bits = 8) or V x D/2 (bits = 4: byte b holds q of
+    weight 2b in its low nibble, of 2b + 1 in its high nibble); scales and
+    biases: float32, V x (D / group). Step by step as the formula reads: the
+    codes as float32, one float32 product, one float32 sum, one rounding to
+    bf16.
+    """
+    c = np.asarray(codes.cpu() if hasattr(codes, "cpu") else codes, dtype=np.uint8)
+    sc = np.asarray(scales.cpu() if hasattr(scales, "cpu") else scales, dtype=np.float32)
+    bi = np.asarray(biases.cpu() if hasattr(biases, "cpu") else biases, dtype=np.float32)
+    if bits == 8:
+        q = c
+    elif bits == 4:
+        q = np.empty((c.shape[0], c.shape[1] * 2), dtype=np.uint8)
+        q[:, 0::2] = c & 0x0F
+        q[:, 1::2] = c >> 4
+    else:
+        raise ValueError("bits must be 4 or 8")
+    V, D = q.shape
+    if group <= 0 or D % group or sc.shape != (V, D // group) or bi.shape != (V, D // group):
+        raise ValueError("group must divide D; scales and biases must be V x D/group")
+    s_full = np.repeat(sc, group, axis=1)
+    b_full = np.repeat(bi, group, axis=1)
+    prod = q.astype(np.float32) * s_full          # float32 * float32 -> one rounding
+    w32 = (prod + b_full).astype(np.float32)      # float32 + float32 -> one rounding
+    return _bf16_rne_bits(w32)
 

@@ -205,3 +205,47 @@ def test_python_binding_validates_shapes(flce):
         flce.flce_forward(H, W, y)            # CPU tensors are refused
     with pytest.raises(ValueError):
         flce._check_inputs(H.cuda() if torch.cuda.is_available() else H, W, y)
+
+
+def test_quant_arguments_rejected_before_any_launch(flce):
+    lib = flce._lib
+    buf = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first
+    odd = ctypes.c_void_p(4096 + 4)
+    need = flce.flce_forward_quant_workspace_bytes(4, 64, 100, 8, 32)
+    assert need > 0
+
+    def q(H=buf, c=buf, s=buf, b=buf, y=buf, N=4, D=64, V=100, bits=8, group=32, loss=buf, lse=None,
+          ws=buf, nb=need):
+        return lib.flce_forward_quant(H, c, s, b, y, N, D, V, bits, group, loss, lse, ws, nb, None)
+
+    assert q(bits=3) == flce.FLCE_ERR_UNSUPPORTED
+    assert q(bits=16) == flce.FLCE_ERR_UNSUPPORTED
+    assert q(group=12) == flce.FLCE_ERR_UNSUPPORTED        # not a multiple of 8
+    assert q(group=128) == flce.FLCE_ERR_UNSUPPORTED       # does not divide D
+    assert q(D=0) == flce.FLCE_ERR_INVALID_ARG
+    assert q(N=-1) == flce.FLCE_ERR_INVALID_ARG
+    for name in ("H", "c", "s", "b", "y", "loss", "ws"):
+        assert q(**{name: None}) == flce.FLCE_ERR_INVALID_ARG, name
+    assert q(c=odd) == flce.FLCE_ERR_INVALID_ARG           # codes need 16-byte alignment
+    assert q(H=odd) == flce.FLCE_ERR_INVALID_ARG
+    assert q(nb=need - 1) == flce.FLCE_ERR_INVALID_ARG
+    assert q(N=0) == flce.FLCE_OK                          # nothing to do, nothing read
+
+
+def test_quant_workspace_layout(flce):
+    """One bf16 slice of Vs rows (a multiple of 3072, near 256 MiB) plus the
+    partial states of every slice's chunks and the target logits."""
+    def up(x, m=256):
+        return (x + m - 1) // m * m
+
+    for N, D, V in [(8192, 4096, 151936), (64, 16384, 13000), (300, 256, 5003), (7, 65536, 7000)]:
+        vs = max(3072, int(256 * 2 ** 20 / (D * 2)) // 3072 * 3072)
+        vs = min(vs, V)
+        slices = -(-V // vs)
+        last = V - (slices - 1) * vs
+        C = (slices - 1) * flce.flce_get_plan(N, D, vs, "bf16")["chunks"] + \
+            flce.flce_get_plan(N, D, last, "bf16")["chunks"]
+        want = up(vs * D * 2) + 2 * up(C * N * 4) + up(N * 4)
+        for bits, group in ((8, 64), (4, 128)):
+            assert flce.flce_forward_quant_workspace_bytes(N, D, V, bits, group) == want, (N, D, V, bits)
+    assert flce.flce_forward_quant_workspace_bytes(0, 64, 100, 8, 32) == 0

@@ -1,0 +1,101 @@
+"""The quantised-head forward (flce_forward_quant) on the GPU.
+
+The dequantised bf16 weights the library leaves in its workspace must equal
+oracle.dequantize bit for bit; a vocabulary that fits one slice must give the
+same bits as flce_forward on those weights; and several slices must match
+the oracle (dequantize, then the float64 forward) on every row, with targets
+on every slice boundary.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import check_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_cross_entropy_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def _as_bf16(bits16):
+    return torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("bits,group,D", [(8, 64, 256), (4, 32, 256), (4, 256, 256),
+                                          (8, 8, 264), (4, 16, 272)])
+def test_single_slice_dequant_bits_and_dense_equality(bits, group, D):
+    """Several bit widths and group sizes, including D = 264 and 272 (groups of 8
+    and 16: 33 and 17 groups a row)."""
+    import linear_cross_entropy_amd as flce
+    N, V = 300, 5003
+    print(f"[quant] N={N} D={D} V={V} bits={bits} group={group}", flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(N, D, V, bits, group, seed=bits + group, device=DEV)
+    # a few rows where two float32 roundings and a fused multiply-add differ
+    third = torch.tensor(1.0, dtype=torch.float32) / torch.tensor(3.0, dtype=torch.float32)
+    scales[:3] = third.item()
+    biases[:3] = -1.0
+    if bits == 8:
+        codes[:3] = 3
+    else:
+        codes[:3] = 0x33
+    nbytes = flce.flce_forward_quant_workspace_bytes(N, D, V, bits, group)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    loss, lse = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group, workspace=ws)
+    torch.cuda.synchronize()
+    ref_bits = oracle.dequantize(codes.cpu(), scales.cpu(), biases.cpu(), bits, group)
+    got_bits = ws[:V * D * 2].cpu().numpy().view(np.uint16).reshape(V, D)
+    bad = np.nonzero(got_bits != ref_bits)
+    assert bad[0].size == 0, f"dequantised weight ({bad[0][0]}, {bad[1][0]}) differs from the oracle"
+    assert np.all(ref_bits[:3] == 0)                     # the rows above: exactly 0, not 2.98e-8
+    W = _as_bf16(ref_bits).to(DEV)
+    loss_d, lse_d = flce.flce_forward(H, W, y)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, loss_d) and torch.equal(lse, lse_d)
+    rl, rs, _ = oracle.forward(H.cpu(), _as_bf16(ref_bits), y.cpu())
+    check_close(lse.cpu().numpy(), rs, torch.bfloat16, "quant lse")
+    check_close(loss.cpu().numpy(), rl, torch.bfloat16, "quant loss")
+
+
+@pytest.mark.parametrize("bits,group", [(8, 128), (4, 64)])
+def test_several_slices_against_the_oracle(bits, group):
+    """D = 16384 gives 6144-row slices: V = 13000 runs as 6144 + 6144 + 712,
+    with targets on both sides of every slice boundary and one ignored row."""
+    import linear_cross_entropy_amd as flce
+    N, D, V = 64, 16384, 13000
+    print(f"[quant] N={N} D={D} V={V} bits={bits} group={group}", flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(N, D, V, bits, group, seed=97 + bits, device=DEV,
+                                                       w_std=1.0 / np.sqrt(D))
+    marks = [0, 6143, 6144, 6145, 12287, 12288, 12999, -1]
+    y[:len(marks)] = torch.tensor(marks, dtype=torch.int32, device=DEV)
+    loss, lse = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group)
+    loss2, lse2 = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group)
+    torch.cuda.synchronize()
+    same = torch.equal(loss.view(torch.int32), loss2.view(torch.int32)) and \
+        torch.equal(lse.view(torch.int32), lse2.view(torch.int32))   # bit patterns: the ignored row is NaN
+    assert same, "second call differs"
+    ref_bits = oracle.dequantize(codes.cpu(), scales.cpu(), biases.cpu(), bits, group)
+    rl, rs, _ = oracle.forward(H.cpu(), _as_bf16(ref_bits), y.cpu())
+    e1 = check_close(lse.cpu().numpy(), rs, torch.bfloat16, "quant slices lse")
+    e2 = check_close(loss.cpu().numpy(), rl, torch.bfloat16, "quant slices loss")
+    assert np.isnan(loss[len(marks) - 1].item())
+    print(f"[quant] max |d| lse {e1:.3e} loss {e2:.3e}", flush=True)
+
+
+def test_binding_rejects_bad_formats():
+    import linear_cross_entropy_amd as flce
+    H, codes, scales, biases, y = workloads.make_quant(8, 64, 100, 8, 32, seed=3, device=DEV)
+    with pytest.raises(ValueError):
+        flce.flce_forward_quant(H, codes, scales, biases, y, 3, 32)
+    with pytest.raises(ValueError):
+        flce.flce_forward_quant(H, codes, scales, biases, y, 8, 24)
+    with pytest.raises(ValueError):
+        flce.flce_forward_quant(H, codes[:, :32].contiguous(), scales, biases, y, 8, 32)

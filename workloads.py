@@ -160,6 +160,33 @@ def make_custom(N: int, D: int, V: int, dtype: str = "bf16", seed: int = 0, devi
     return H, W, y
 
 
+STREAM_CODES, STREAM_SCALES, STREAM_BIASES = 4, 5, 6
+
+
+def make_quant(N: int, D: int, V: int, bits: int, group: int, seed: int = 0, device="cpu",
+               w_std: float = 0.02, target_kind: str = "uniform"):
+    """Seeded inputs for a quantised head: H (N x D, bf16, N(0,1)), codes
+    uniform over [0, 2^bits) stored as uint8 (V x D at 8 bits, V x D/2 at 4
+    bits: byte b holds code 2b in its low nibble and 2b+1 in its high one),
+    float32 scales and biases per group of ``group`` weights (V x D/group),
+    and int32 targets. Scales are w_std * sqrt(12) / 2^bits times U(0.5, 1.5)
+    and biases minus scale * (2^bits - 1) / 2 times U(0.9, 1.1), so that the
+    weights they describe are centred with a spread of about w_std."""
+    base = 7919 * (seed + 1)
+    H = normal_matrix(N, D, 1.0, torch.bfloat16, device, base + STREAM_H)
+    levels = 1 << bits
+    g = _gen(device, base + STREAM_CODES)
+    q = torch.randint(0, levels, (V, D), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    codes = q if bits == 8 else (q[:, 0::2] | (q[:, 1::2] << 4)).contiguous()
+    G = D // group
+    gs = _gen(device, base + STREAM_SCALES)
+    scale = (torch.rand(V, G, generator=gs, device=device) + 0.5) * (w_std * 12.0 ** 0.5 / levels)
+    gb = _gen(device, base + STREAM_BIASES)
+    bias = -scale * ((levels - 1) / 2.0) * (torch.rand(V, G, generator=gb, device=device) * 0.2 + 0.9)
+    y = targets(N, V, target_kind, base + STREAM_Y).to(device)
+    return H, codes, scale.contiguous(), bias.contiguous(), y
+
+
 def subset_rows(N: int, count: int = 256, seed: int = 12345) -> torch.Tensor:
     """Row sample used where the oracle cannot take every row: the first and
     last count//8 rows plus seeded random rows in between (sorted, unique)."""
