@@ -202,7 +202,9 @@ def bench_backward(args, w):
 def bench_quant(args, w):
     """The forward with a quantised head of the workload's shape: each step is
     one flce_forward_quant (dequantisation slice by slice, the partials kernel
-    per slice, one merge), timed whole with HIP events on the launch stream."""
+    per slice, one merge), timed whole with HIP events on the launch stream.
+    With --backward, each step is one flce_backward_quant (dH of the mean
+    loss for the frozen head, given the forward's lse): 2 x 2 N V D FLOP."""
     import torch
     import linear_cross_entropy_amd as flce
     import workloads
@@ -221,6 +223,24 @@ def bench_quant(args, w):
         flce.flce_forward_quant(H, codes, scales, biases, y, args.quant, args.group, workspace=ws,
                                 loss=loss, lse=lse, stream=stream)
 
+    flops = w.flops
+    what = "fwd"
+    kernel = "flce_forward_quant (all launches: dequantisation per slice, partials per slice, merge)"
+    if args.backward:
+        step()
+        g = torch.full((w.N,), 1.0 / w.N, dtype=torch.float32, device=dev)
+        dH = torch.empty(w.N, w.D, dtype=torch.float32, device=dev)
+        ws = torch.empty(flce.flce_backward_quant_workspace_bytes(w.N, w.D, w.V, args.quant, args.group),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            flce.flce_backward_quant(H, codes, scales, biases, y, lse, g, args.quant, args.group, workspace=ws,
+                                     dH=dH, stream=stream)
+        flops = 2 * w.flops
+        what = "backward (dH, frozen head)"
+        kernel = ("flce_backward_quant (all launches: per slice dequantisation, transpose, dZ pass, dH product; "
+                  "partial-sum add)")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -234,10 +254,10 @@ def bench_quant(args, w):
     wall = time.perf_counter() - t0
     each = [a.elapsed_time(b) for a, b in ev]
     avg = sum(each) / len(each)
-    achieved = w.flops / (avg * 1e-3) / 1e12
+    achieved = flops / (avg * 1e-3) / 1e12
     head_bytes = codes.numel() + 2 * scales.numel() * 4
     result = {
-        "metric": f"tokens/s + % bf16 MFMA peak, fused LCE fwd with a {args.quant}-bit head "
+        "metric": f"tokens/s + % bf16 MFMA peak, fused LCE {what} with a {args.quant}-bit head "
                   f"N={w.N} D={w.D} V={w.V}",
         "value": w.N * args.steps / wall,
         "unit": "tokens/s",
@@ -255,19 +275,19 @@ def bench_quant(args, w):
                    "head_bytes": head_bytes, "workspace_bytes": ws.numel()},
         "roofline": {
             "bound": "mfma",
-            "kernel": "flce_forward_quant (all launches: dequantisation per slice, partials per slice, merge)",
+            "kernel": kernel,
             "achieved": achieved,
             "peak": PEAK_TFLOPS["bf16"],
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_TFLOPS["bf16"],
             "traffic": None,
-            "algorithmic_flop_per_launch": w.flops,
+            "algorithmic_flop_per_launch": flops,
             "kernel_ms_avg": avg,
             "kernel_ms_median": sorted(each)[len(each) // 2],
             "kernel_ms_min": min(each),
             "kernel_ms_each": [round(t, 4) for t in each],
         },
-        "outputs_finite": bool(torch.isfinite(loss).all().item()),
+        "outputs_finite": bool(torch.isfinite(dH if args.backward else loss).all().item()),
         "cpu_baseline": None,
     }
     print(json.dumps(result))
@@ -288,7 +308,8 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (flce_backward, given the forward's lse) instead of the forward")
     ap.add_argument("--quant", type=int, default=0, choices=(0, 4, 8), metavar="BITS",
-                    help="time flce_forward_quant with a BITS-bit head of the workload's shape instead")
+                    help="time flce_forward_quant (with --backward: flce_backward_quant) with a BITS-bit head "
+                         "of the workload's shape instead")
     ap.add_argument("--group", type=int, default=64, help="weights per scale/bias group with --quant")
     args = ap.parse_args()
 
@@ -310,11 +331,11 @@ def main():
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    if args.backward:
-        bench_backward(args, w)
-        return
     if args.quant:
         bench_quant(args, w)
+        return
+    if args.backward:
+        bench_backward(args, w)
         return
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)

@@ -202,6 +202,32 @@ int flce_forward_quant(const void* H, const uint8_t* codes, const float* scales,
  * unsupported shape). */
 size_t flce_forward_quant_workspace_bytes(int64_t N, int64_t D, int64_t V, int bits, int group);
 
+/*
+ * Backward of flce_forward_quant for a frozen head: dH (N x D, float32,
+ * 16-byte aligned, fully overwritten) of sum_i g_i loss_i, where the loss is
+ * the one flce_forward_quant defines and lse is its lse_out for the same
+ * inputs. The head (codes, scales, biases) gets no gradient. Computed as
+ * flce_backward computes dH for the dequantised bf16 W (dZ rounded to bf16,
+ * float32 accumulation), one vocabulary slice at a time: the slice's dH
+ * contributions are float32 partial products added in slice order at the
+ * end (deterministic); a vocabulary that fits one slice gives the same bits
+ * as flce_backward's dH on the dequantised W.
+ *   - workspace: flce_backward_quant_workspace_bytes(N, D, V, bits, group)
+ *     bytes, 256-byte aligned: one dequantised slice, its transpose, dZ of
+ *     all rows for the slice (transposed), and the partial products. Allocates
+ *     nothing. N == 0 enqueues nothing.
+ *   - Format, alignment and status codes as for flce_forward_quant and
+ *     flce_backward.
+ */
+int flce_backward_quant(const void* H, const uint8_t* codes, const float* scales, const float* biases,
+                        const int32_t* targets, const float* lse, const float* grad_loss,
+                        int64_t N, int64_t D, int64_t V, int bits, int group, float* dH,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes flce_backward_quant needs (0 for N == 0 or an invalid or
+ * unsupported shape). */
+size_t flce_backward_quant_workspace_bytes(int64_t N, int64_t D, int64_t V, int bits, int group);
+
 /* Tile plan for a shape; FLCE_ERR_INVALID_ARG/UNSUPPORTED as flce_forward. */
 int flce_get_plan(int64_t N, int64_t D, int64_t V, int dtype, flce_plan_t* plan);
 

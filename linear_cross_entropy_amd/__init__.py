@@ -18,6 +18,9 @@ device memory and the stream. The functions keep the C names:
     linear_cross_entropy(H, W, targets) -> loss   (torch.autograd: gradients for H and W)
     flce_forward_quant(H, codes, scales, biases, targets, bits, group, workspace=None, loss=None, lse=None, stream=None)
     flce_forward_quant_workspace_bytes(N, D, V, bits, group) -> int
+    flce_backward_quant(H, codes, scales, biases, targets, lse, grad_loss, bits, group, workspace=None, dH=None, stream=None)
+    flce_backward_quant_workspace_bytes(N, D, V, bits, group) -> int
+    linear_cross_entropy_quant(H, codes, scales, biases, targets, bits, group) -> loss   (gradient for H)
 
 The operation (page "Een gefuseerde forward-kernel
 voor lineaire cross-entropy op Apple-GPU's", section 1): with logits Z = H W^T, lse_i = logsumexp(Z_i) and
@@ -71,6 +74,11 @@ _lib.flce_forward_quant.argtypes = [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _
 _lib.flce_forward_quant.restype = _i32
 _lib.flce_forward_quant_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
 _lib.flce_forward_quant_workspace_bytes.restype = _sz
+_lib.flce_backward_quant.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _sz,
+                                     _vp]
+_lib.flce_backward_quant.restype = _i32
+_lib.flce_backward_quant_workspace_bytes.argtypes = [_i64, _i64, _i64, _i32, _i32]
+_lib.flce_backward_quant_workspace_bytes.restype = _sz
 _lib.flce_status_string.argtypes = [_i32]
 _lib.flce_status_string.restype = ctypes.c_char_p
 _lib.flce_version.argtypes = []
@@ -94,7 +102,8 @@ _lib.flce_get_plan.restype = _i32
 EXPORTED = ["flce_forward", "flce_forward_ws", "flce_partials", "flce_merge",
             "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version",
             "flce_backward", "flce_backward_workspace_bytes",
-            "flce_forward_quant", "flce_forward_quant_workspace_bytes"]
+            "flce_forward_quant", "flce_forward_quant_workspace_bytes",
+            "flce_backward_quant", "flce_backward_quant_workspace_bytes"]
 
 
 class FlceError(RuntimeError):
@@ -282,11 +291,7 @@ def flce_forward_quant_workspace_bytes(N: int, D: int, V: int, bits: int, group:
     return int(_lib.flce_forward_quant_workspace_bytes(N, D, V, bits, group))
 
 
-def flce_forward_quant(H, codes, scales, biases, targets, bits: int, group: int, workspace=None,
-                       loss=None, lse=None, stream=None):
-    """(loss, lse) for a quantised head: codes (V, D) uint8 at 8 bits or (V, D/2)
-    at 4 bits (two per byte, low nibble first), scales and biases float32
-    (V, D/group); see flce_forward_quant in include/flce.h for the format."""
+def _check_quant(H, codes, scales, biases, targets, bits, group):
     for name, t in (("H", H), ("codes", codes), ("scales", scales), ("biases", biases), ("targets", targets)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous torch.Tensor on a GPU device")
@@ -304,6 +309,15 @@ def flce_forward_quant(H, codes, scales, biases, targets, bits: int, group: int,
             raise ValueError(f"{name} must be float32 of shape ({V}, {D // group})")
     if targets.dtype != torch.int32 or targets.shape != (N,):
         raise ValueError("targets must be int32 of shape (N,)")
+    return N, D, V
+
+
+def flce_forward_quant(H, codes, scales, biases, targets, bits: int, group: int, workspace=None,
+                       loss=None, lse=None, stream=None):
+    """(loss, lse) for a quantised head: codes (V, D) uint8 at 8 bits or (V, D/2)
+    at 4 bits (two per byte, low nibble first), scales and biases float32
+    (V, D/group); see flce_forward_quant in include/flce.h for the format."""
+    N, D, V = _check_quant(H, codes, scales, biases, targets, bits, group)
     dev = H.device
     loss = _out(loss, N, dev, "loss")
     lse = _out(lse, N, dev, "lse")
@@ -318,6 +332,63 @@ def flce_forward_quant(H, codes, scales, biases, targets, bits: int, group: int,
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_forward_quant")
     return loss, lse
+
+
+def flce_backward_quant_workspace_bytes(N: int, D: int, V: int, bits: int, group: int) -> int:
+    return int(_lib.flce_backward_quant_workspace_bytes(N, D, V, bits, group))
+
+
+def flce_backward_quant(H, codes, scales, biases, targets, lse, grad_loss, bits: int, group: int,
+                        workspace=None, dH=None, stream=None):
+    """dH (float32) of sum_i grad_loss[i] * loss_i for the quantised head, which
+    is frozen (no gradient); lse is flce_forward_quant's lse for the same inputs."""
+    N, D, V = _check_quant(H, codes, scales, biases, targets, bits, group)
+    dev = H.device
+    lse = _vec(lse, N, dev, "lse")
+    grad_loss = _vec(grad_loss, N, dev, "grad_loss")
+    dH = _mat(dH, N, D, dev, "dH")
+    if N == 0:
+        return dH
+    nbytes = flce_backward_quant_workspace_bytes(N, D, V, bits, group)
+    if nbytes == 0:
+        raise FlceError(FLCE_ERR_UNSUPPORTED, "flce_backward_quant_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    rc = _lib.flce_backward_quant(_ptr(H), _ptr(codes), _ptr(scales), _ptr(biases), _ptr(targets), _ptr(lse),
+                                  _ptr(grad_loss), N, D, V, bits, group, _ptr(dH), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream_ptr(stream, dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_backward_quant")
+    return dH
+
+
+class LinearCrossEntropyQuant(torch.autograd.Function):
+    """Per-token loss for a quantised head, differentiable in H only (the head
+    is frozen): forward flce_forward_quant, backward flce_backward_quant with
+    the saved lse."""
+
+    @staticmethod
+    def forward(ctx, H, codes, scales, biases, targets, bits, group):
+        loss, lse = flce_forward_quant(H, codes, scales, biases, targets, bits, group)
+        ctx.save_for_backward(H, codes, scales, biases, targets, lse)
+        ctx.bits, ctx.group = bits, group
+        return loss
+
+    @staticmethod
+    def backward(ctx, grad_loss):
+        H, codes, scales, biases, targets, lse = ctx.saved_tensors
+        dH = None
+        if ctx.needs_input_grad[0]:
+            g = grad_loss.to(torch.float32).contiguous()
+            dH = flce_backward_quant(H, codes, scales, biases, targets, lse, g, ctx.bits, ctx.group)
+        return dH, None, None, None, None, None, None
+
+
+def linear_cross_entropy_quant(H, codes, scales, biases, targets, bits: int, group: int):
+    """Per-token loss (float32, (N,)) with a quantised head in the format of
+    flce_forward_quant; differentiable in H. Ignored positions (targets outside
+    [0, V)) are handled as in linear_cross_entropy."""
+    return LinearCrossEntropyQuant.apply(H, codes, scales, biases, targets, bits, group)
 
 
 class LinearCrossEntropy(torch.autograd.Function):

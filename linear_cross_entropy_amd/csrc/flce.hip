@@ -1428,6 +1428,86 @@ int launch_forward_quant(const QuantPlan& qp, const void* H, const uint8_t* code
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+// Backward of the quantised-head forward for a frozen head: dH only. Per
+// vocabulary slice, as in the forward: dequantise, transpose the slice (the
+// dH product's A operand), the dZ pass over all rows for the slice's
+// vocabulary (targets offset by its first row), and the transposed-B dH
+// product over the slice's vocabulary, written as partial products (one per
+// slice, times its own K split); flce_ksum_kernel adds them in slice order.
+struct QuantBwdPlan {
+  QuantPlan q;           // slices and Vs
+  BwdPlan full, last;    // Vp, Np, K split of a full slice and of the last one
+  int parts;             // partial dH products over all slices
+  size_t off_w, off_wt, off_dzt, off_part, ws_bytes;
+};
+
+int make_quant_bwd_plan(int64_t N, int64_t D, int64_t V, int bits, int group, QuantBwdPlan* qb) {
+  int rc;
+  if ((rc = make_quant_plan(N, D, V, bits, group, &qb->q)) != FLCE_OK) return rc;
+  const int64_t v_last = V - (int64_t)(qb->q.slices - 1) * qb->q.Vs;
+  if ((rc = make_bwd_plan(N, D, qb->q.Vs, FLCE_BF16, &qb->full)) != FLCE_OK) return rc;
+  if ((rc = make_bwd_plan(N, D, v_last, FLCE_BF16, &qb->last)) != FLCE_OK) return rc;
+  qb->parts = (qb->q.slices - 1) * qb->full.ksplit + qb->last.ksplit;
+  qb->off_w = 0;
+  qb->off_wt = align_up((size_t)(qb->q.Vs * D * 2));
+  qb->off_dzt = qb->off_wt + align_up((size_t)(D * qb->full.Vp * 2));
+  qb->off_part = qb->off_dzt + align_up((size_t)(qb->full.Vp * qb->full.Np * 2));
+  qb->ws_bytes = qb->off_part + (qb->parts > 1 ? align_up((size_t)qb->parts * (size_t)(N * D) * 4) : 0);
+  return FLCE_OK;
+}
+
+int launch_backward_quant(const QuantBwdPlan& qb, const void* H, const uint8_t* codes, const float* scales,
+                          const float* biases, const int32_t* y, const float* lse, const float* grad, float* dH,
+                          void* ws, hipStream_t stream) {
+  char* base = (char*)ws;
+  __bf16* wbuf = (__bf16*)(base + qb.off_w);
+  char* wt = base + qb.off_wt;
+  char* dzt = base + qb.off_dzt;
+  float* part = (float*)(base + qb.off_part);
+  const QuantPlan& q = qb.q;
+  const size_t code_row = (size_t)(q.bits == 8 ? q.D : q.D / 2);
+  const int64_t groups = q.D / q.group;
+  int64_t p0 = 0;
+  for (int k = 0; k < q.slices; ++k) {
+    const BwdPlan& bp = k + 1 < q.slices ? qb.full : qb.last;
+    const int64_t v0 = (int64_t)k * q.Vs;
+    launch_dequant(q.bits, (int)q.D, q.group, codes + v0 * code_row, scales + v0 * groups, biases + v0 * groups,
+                   bp.V, wbuf, stream);
+    launch_transpose<__bf16>(wbuf, (int)bp.V, (int)q.D, q.D, wt, bp.Vp, (int)bp.Vp, stream);
+    Plan pz, ph;
+    if (make_plan(q.N, q.D, bp.V, FLCE_BF16, &pz) != FLCE_OK ||
+        make_plan(q.N, bp.Vp, q.D, FLCE_BF16, &ph, kTile320) != FLCE_OK)
+      return FLCE_ERR_UNSUPPORTED;
+    TileArgs a = tile_args(pz, H, wbuf);
+    a.y = y;
+    a.v_off = (int)v0;
+    a.lse = lse;
+    a.grad = grad;
+    a.dz = nullptr;
+    a.dzt = dzt;
+    a.dzt_ld = (int)bp.Np;
+    a.dz_rows = (int)bp.Np;
+    a.dz_cols = (int)bp.Vp;
+    FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
+    TileArgs g = tile_args(ph, dzt, wt);
+    g.ldb = (int)bp.Np;
+    g.ldc = (int)q.D;
+    g.ksplit = bp.ksplit;
+    g.ks_per = bp.ks_per;
+    g.C = qb.parts > 1 ? part + (size_t)p0 * (size_t)(q.N * q.D) : dH;
+    Plan phs = ph;
+    phs.grid = ph.row_blocks * ph.chunks * bp.ksplit;
+    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, phs, g, stream);
+    p0 += bp.ksplit;
+  }
+  if (qb.parts > 1) {
+    const int64_t n4 = q.N * q.D / 4;
+    hipLaunchKernelGGL(flce_ksum_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 2048)), dim3(256), 0,
+                       stream, (const float*)part, qb.parts, n4, dH);
+  }
+  return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1572,6 +1652,32 @@ int flce_forward_quant(const void* H, const uint8_t* codes, const float* scales,
   if (!workspace || workspace_bytes < qp.ws_bytes || !aligned(workspace, kAlign)) return FLCE_ERR_INVALID_ARG;
   return launch_forward_quant(qp, H, codes, scales, biases, targets, loss_out, lse_out, workspace,
                               (hipStream_t)stream);
+}
+
+size_t flce_backward_quant_workspace_bytes(int64_t N, int64_t D, int64_t V, int bits, int group) {
+  QuantBwdPlan qb;
+  if (N == 0 || make_quant_bwd_plan(N, D, V, bits, group, &qb) != FLCE_OK) return 0;
+  return qb.ws_bytes;
+}
+
+int flce_backward_quant(const void* H, const uint8_t* codes, const float* scales, const float* biases,
+                        const int32_t* targets, const float* lse, const float* grad_loss, int64_t N, int64_t D,
+                        int64_t V, int bits, int group, float* dH, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (N == 0) {
+    QuantPlan q;
+    return make_quant_plan(N, D, V, bits, group, &q);
+  }
+  QuantBwdPlan qb;
+  int rc = make_quant_bwd_plan(N, D, V, bits, group, &qb);
+  if (rc != FLCE_OK) return rc;
+  if (!H || !codes || !scales || !biases || !targets || !lse || !grad_loss || !dH) return FLCE_ERR_INVALID_ARG;
+  if (!aligned(H, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(biases, 4) ||
+      !aligned(targets, 4) || !aligned(lse, 4) || !aligned(grad_loss, 4) || !aligned(dH, 16))
+    return FLCE_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < qb.ws_bytes || !aligned(workspace, kAlign)) return FLCE_ERR_INVALID_ARG;
+  return launch_backward_quant(qb, H, codes, scales, biases, targets, lse, grad_loss, dH, workspace,
+                               (hipStream_t)stream);
 }
 
 }  // extern "C"

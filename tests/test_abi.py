@@ -249,3 +249,31 @@ def test_quant_workspace_layout(flce):
         for bits, group in ((8, 64), (4, 128)):
             assert flce.flce_forward_quant_workspace_bytes(N, D, V, bits, group) == want, (N, D, V, bits)
     assert flce.flce_forward_quant_workspace_bytes(0, 64, 100, 8, 32) == 0
+
+
+def test_quant_backward_arguments_rejected_before_any_launch(flce):
+    lib = flce._lib
+    buf = ctypes.c_void_p(4096)       # never dereferenced: every call below fails validation first
+    odd = ctypes.c_void_p(4096 + 8)
+    need = flce.flce_backward_quant_workspace_bytes(4, 64, 100, 8, 32)
+    assert need > 0
+
+    def qb(H=buf, c=buf, s=buf, b=buf, y=buf, lse=buf, g=buf, N=4, D=64, V=100, bits=8, group=32, dH=buf,
+           ws=buf, nb=need):
+        return lib.flce_backward_quant(H, c, s, b, y, lse, g, N, D, V, bits, group, dH, ws, nb, None)
+
+    assert qb(bits=5) == flce.FLCE_ERR_UNSUPPORTED
+    assert qb(group=20) == flce.FLCE_ERR_UNSUPPORTED
+    for name in ("H", "c", "s", "b", "y", "lse", "g", "dH", "ws"):
+        assert qb(**{name: None}) == flce.FLCE_ERR_INVALID_ARG, name
+    assert qb(dH=odd) == flce.FLCE_ERR_INVALID_ARG         # 16-byte dH stores
+    assert qb(nb=need - 1) == flce.FLCE_ERR_INVALID_ARG
+    assert qb(N=0) == flce.FLCE_OK
+    assert flce.flce_backward_quant_workspace_bytes(0, 64, 100, 8, 32) == 0
+    # one slice, its transpose, dZ^T of the slice, and (when there is more than one) the partial dH products
+    up = lambda x, m=256: (x + m - 1) // m * m
+    N, D, V = 8192, 4096, 151936
+    vs, Np = 30720, 8192
+    base = up(vs * D * 2) + up(D * vs * 2) + up(vs * Np * 2)
+    got = flce.flce_backward_quant_workspace_bytes(N, D, V, 4, 64)
+    assert got == base + up(5 * N * D * 4)                 # five slices, no split within a slice

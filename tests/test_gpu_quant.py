@@ -99,3 +99,67 @@ def test_binding_rejects_bad_formats():
         flce.flce_forward_quant(H, codes, scales, biases, y, 8, 24)
     with pytest.raises(ValueError):
         flce.flce_forward_quant(H, codes[:, :32].contiguous(), scales, biases, y, 8, 32)
+
+
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 32)])
+def test_backward_single_slice_equals_the_dense_backward(bits, group):
+    """dH for a vocabulary that fits one slice: the same bits as flce_backward's
+    dH on the dequantised bf16 head, and the oracle's dH within the backward
+    bound."""
+    import linear_cross_entropy_amd as flce
+    from parity import check_bwd
+    N, D, V = 300, 256, 5003
+    print(f"[quant bwd] N={N} D={D} V={V} bits={bits} group={group}", flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(N, D, V, bits, group, seed=11 + bits, device=DEV)
+    g = torch.linspace(0.5, 1.5, N, dtype=torch.float32, device=DEV)
+    _, lse = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group)
+    dH = flce.flce_backward_quant(H, codes, scales, biases, y, lse, g, bits, group)
+    torch.cuda.synchronize()
+    ref_bits = oracle.dequantize(codes.cpu(), scales.cpu(), biases.cpu(), bits, group)
+    W = _as_bf16(ref_bits).to(DEV)
+    dH_d, _ = flce.flce_backward(H, W, y, lse, g)
+    torch.cuda.synchronize()
+    assert torch.equal(dH, dH_d)
+    ref = oracle.backward(H.cpu(), _as_bf16(ref_bits), y.cpu(), g.cpu(), want_dW=False)
+    check_bwd(dH.cpu().numpy(), ref["dH"], ref["dH_abs"], torch.bfloat16, V, "quant bwd dH")
+
+
+@pytest.mark.parametrize("bits,group", [(8, 128), (4, 64)])
+def test_backward_several_slices_against_the_oracle(bits, group):
+    """Three vocabulary slices (D = 16384, V = 13000), each dH product further
+    split over its vocabulary (64 rows leave CUs idle): nine partial products
+    added in order. Targets on the slice boundaries and one outside [0, V)."""
+    import linear_cross_entropy_amd as flce
+    from parity import check_bwd
+    N, D, V = 64, 16384, 13000
+    print(f"[quant bwd] N={N} D={D} V={V} bits={bits} group={group}", flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(N, D, V, bits, group, seed=31 + bits, device=DEV,
+                                                       w_std=1.0 / np.sqrt(D))
+    marks = [0, 6143, 6144, 12287, 12288, 12999, -1]
+    y[:len(marks)] = torch.tensor(marks, dtype=torch.int32, device=DEV)
+    g = torch.linspace(0.25, 1.75, N, dtype=torch.float32, device=DEV)
+    _, lse = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group)
+    dH = flce.flce_backward_quant(H, codes, scales, biases, y, lse, g, bits, group)
+    dH2 = flce.flce_backward_quant(H, codes, scales, biases, y, lse, g, bits, group)
+    torch.cuda.synchronize()
+    assert torch.equal(dH, dH2), "second call differs"
+    ref_bits = oracle.dequantize(codes.cpu(), scales.cpu(), biases.cpu(), bits, group)
+    ref = oracle.backward(H.cpu(), _as_bf16(ref_bits), y.cpu(), g.cpu(), want_dW=False)
+    e, rel = check_bwd(dH.cpu().numpy(), ref["dH"], ref["dH_abs"], torch.bfloat16, V, "quant slices bwd dH")
+    print(f"[quant bwd] max |d| {e:.3e}, relative Frobenius error {rel:.2e}", flush=True)
+
+
+def test_autograd_quant_head():
+    import linear_cross_entropy_amd as flce
+    N, D, V = 200, 128, 3001
+    H0, codes, scales, biases, y = workloads.make_quant(N, D, V, 4, 32, seed=71, device=DEV)
+    weights = torch.linspace(-1.0, 2.0, N, dtype=torch.float32, device=DEV)
+    H = H0.clone().requires_grad_(True)
+    loss = flce.linear_cross_entropy_quant(H, codes, scales, biases, y, 4, 32)
+    (loss * weights).sum().backward()
+    torch.cuda.synchronize()
+    loss_d, lse_d = flce.flce_forward_quant(H0, codes, scales, biases, y, 4, 32)
+    dH_d = flce.flce_backward_quant(H0, codes, scales, biases, y, lse_d, weights.contiguous(), 4, 32)
+    torch.cuda.synchronize()
+    assert torch.equal(loss.detach(), loss_d)
+    assert H.grad.dtype == torch.bfloat16 and torch.equal(H.grad, dH_d.to(torch.bfloat16))
