@@ -277,3 +277,44 @@ def test_quant_backward_arguments_rejected_before_any_launch(flce):
     base = up(vs * D * 2) + up(D * vs * 2) + up(vs * Np * 2)
     got = flce.flce_backward_quant_workspace_bytes(N, D, V, 4, 64)
     assert got == base + up(5 * N * D * 4)                 # five slices, no split within a slice
+
+
+def test_header_is_plain_c_and_links(flce, tmp_path):
+    """include/flce.h compiles as strict C11 (the boundary is meant for C
+    callers, not only C++), and a C program that takes the address of every
+    declared entry point links against the built library and runs the host-side
+    ones (no GPU needed: planning, sizes, status text, version)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    names = declared_functions()
+    lib_dir = os.path.dirname(flce.LIB_PATH)
+    src = tmp_path / "uses_flce.c"
+    src.write_text(
+        '#include "flce.h"\n#include <stdio.h>\n'
+        "typedef void (*any_fn)(void);\n"
+        "static const any_fn entry_points[] = {\n"
+        + "".join(f"  (any_fn){n},\n" for n in names)
+        + "};\n"
+        "int main(void) {\n"
+        "  flce_plan_t plan;\n"
+        "  int rc = flce_get_plan(8192, 4096, 151936, FLCE_BF16, &plan);\n"
+        '  printf("%d %d %d %d %zu %s %d\\n", (int)(sizeof entry_points / sizeof entry_points[0]), rc,\n'
+        "         plan.tile_vocab, plan.chunks, flce_workspace_bytes(8192, 4096, 151936, FLCE_BF16),\n"
+        "         flce_status_string(FLCE_ERR_UNSUPPORTED), flce_version());\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "uses_flce"
+    include_dir = os.path.dirname(HEADER)
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic", "-Wno-cast-function-type",
+           "-I", include_dir, str(src), "-L", lib_dir, "-lflce", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    count, rc, tile, chunks, ws, *rest = out.stdout.split()
+    plan = flce.flce_get_plan(8192, 4096, 151936, "bf16")
+    assert int(count) == len(names) and int(rc) == 0
+    assert int(tile) == plan["tile_vocab"] and int(chunks) == plan["chunks"]
+    assert int(ws) == flce.flce_workspace_bytes(8192, 4096, 151936, "bf16")
+    assert int(rest[-1]) == flce.flce_version()
