@@ -163,3 +163,29 @@ def test_autograd_quant_head():
     torch.cuda.synchronize()
     assert torch.equal(loss.detach(), loss_d)
     assert H.grad.dtype == torch.bfloat16 and torch.equal(H.grad, dH_d.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("N,D,V,bits,group", [
+    (1, 8, 1, 4, 8),            # one token, one vocabulary row, the smallest D and group
+    (3, 16, 17, 8, 8),
+    (257, 1024, 3073, 4, 128),  # ragged rows and vocabulary, one slice
+    (5, 65536, 6500, 8, 64),    # 3072-row slices (the minimum) and a ragged last one
+], ids=lambda v: str(v))
+def test_degenerate_and_ragged_quant_shapes(N, D, V, bits, group):
+    import linear_cross_entropy_amd as flce
+    from parity import check_bwd
+    print(f"[quant edge] N={N} D={D} V={V} bits={bits} group={group}", flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(N, D, V, bits, group, seed=N + V, device=DEV,
+                                                       w_std=1.0 / np.sqrt(D))
+    y[0] = V - 1
+    loss, lse = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group)
+    g = torch.linspace(0.5, 1.5, N, dtype=torch.float32, device=DEV)
+    dH = flce.flce_backward_quant(H, codes, scales, biases, y, lse, g, bits, group)
+    torch.cuda.synchronize()
+    ref_bits = oracle.dequantize(codes.cpu(), scales.cpu(), biases.cpu(), bits, group)
+    Wq = _as_bf16(ref_bits)
+    rl, rs, _ = oracle.forward(H.cpu(), Wq, y.cpu())
+    check_close(lse.cpu().numpy(), rs, torch.bfloat16, "quant edge lse")
+    check_close(loss.cpu().numpy(), rl, torch.bfloat16, "quant edge loss")
+    ref = oracle.backward(H.cpu(), Wq, y.cpu(), g.cpu(), want_dW=False)
+    check_bwd(dH.cpu().numpy(), ref["dH"], ref["dH_abs"], torch.bfloat16, V, "quant edge dH")
