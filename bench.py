@@ -203,7 +203,19 @@ def bench_backward(args, w):
         result["cpu_baseline"] = cpu_baseline_backward(H, W, y, g, w, args.cpu_seconds, args.cpu_max_rows)
     else:
         result["cpu_baseline"] = None
+    result["env"] = device_env()
     print(json.dumps(result), flush=True)
+
+
+def device_env():
+    """What the line was measured on: ROCm (HIP) version, GPU architecture and
+    compute-unit count as the runtime reports them, and the host threads the
+    CPU oracle may use."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"hip": torch.version.hip, "torch": torch.__version__, "device": props.name,
+            "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "hbm_bytes": props.total_memory, "host_threads": os.cpu_count()}
 
 
 def bench_quant(args, w):
@@ -297,6 +309,7 @@ def bench_quant(args, w):
         "outputs_finite": bool(torch.isfinite(dH if args.backward else loss).all().item()),
         "cpu_baseline": None,
     }
+    result["env"] = device_env()
     print(json.dumps(result))
 
 
@@ -430,6 +443,7 @@ def main():
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
     else:
         result["cpu_baseline"] = None
+    result["env"] = device_env()
     print(json.dumps(result), flush=True)
 
 
