@@ -17,10 +17,18 @@
  * (2*C + 1)*N floats, where C (the number of vocabulary chunks per row
  * block) is at most a few hundred.
  *
+ * Entry points: the forward (flce_forward, flce_forward_ws, and its two
+ * launches flce_partials and flce_merge); its backward (flce_backward: dH and
+ * dW from the forward's lse, regenerating the logits); the forward and a
+ * frozen head's backward with the head stored quantised (flce_forward_quant,
+ * flce_backward_quant); workspace sizes, the tile plan, status text and the
+ * version.
+ *
  * Conventions for every entry point:
  *   - H, W, targets, loss_out, lse_out, workspace (and, for the backward,
- *     lse, grad_loss, dH and dW) are DEVICE pointers owned by the caller. The library never frees them and keeps none of them
- *     after the call returns.
+ *     lse, grad_loss, dH and dW; for a quantised head, codes, scales and
+ *     biases) are DEVICE pointers owned by the caller. The library never
+ *     frees them and keeps none of them after the call returns.
  *   - H is N x D and W is V x D, row-major and dense (row stride D elements),
  *     both of `dtype`. They must be 16-byte aligned and D * sizeof(element)
  *     must be a multiple of 16 (D % 8 == 0 for bf16, D % 4 == 0 for fp32).
