@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -58,6 +59,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr f32x16 kZero16 = {};
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
@@ -410,16 +412,13 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // ---- per-lane online state for the NB token columns this lane holds.
   // 32x32 MFMA output layout: lane l holds column l%32 and, in register r,
   // row 8*(r/4) + 4*(l/32) + r%4 of the 32x32 tile.
-  float m_run[NB], s_run[NB], zt[NB];
-  bool zhit[NB];
+  float m_run[NB], s_run[NB];
   int ytok[NB];
   float l2tok[NB], gtok[NB];  // kDz: lse * log2(e) and the upstream gradient of each token
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m_run[nb] = kNegInf;
     s_run[nb] = 0.f;
-    zt[nb] = 0.f;
-    zhit[nb] = false;
     const int tok = t0 + wt * WT + nb * 32 + (lane & 31);
     ytok[nb] = -1;
     l2tok[nb] = 0.f;
@@ -528,95 +527,106 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // the higher priority from the barrier through the stage's last steps (and
   // a tile's epilogue) and drops it when the next stage's main steps begin.
   const bool young = C::YOUNG_PRIO && wave >= C::NW / 2;
-  int ks = 0, tile = 0;
-  for (int g = 0; g < total; ++g) {
-    const char* sb = smem + (g & 1) * kStageBytes;
-    const char* sn = smem + ((g + 1) & 1) * kStageBytes;  // at g == total - 1: read and ignored
-    if (ks == 0) {
+  int tile = 0;
+  // One stage g of the chunk (stage g lives in LDS buffer g & 1 and takes QN
+  // MFMA steps). A tile's first stage is a separate copy (first_stage true),
+  // so that its first k-block can start from a zero accumulator.
+  auto stage = [&](auto first_stage, const int g) {
+      const char* sb = smem + (g & 1) * kStageBytes;
+      const char* sn = smem + ((g + 1) & 1) * kStageBytes;  // at g == total - 1: read and ignored
+      const bool more1 = g + 1 < total;
+      if (young) __builtin_amdgcn_s_setprio(0);
+      // The main steps [q0, q1): each W fragment's matrix instructions, then the
+      // reads its slot (and, at a k-block's start, the idle H set) can take,
+      // then a load, kept in that order by the scheduling barriers. With kFirst
+      // (the first stage of a tile) the first k-block's matrix instructions take
+      // a zero accumulator (an inline constant), which starts the tile without
+      // clearing its accumulators.
+      auto main_steps = [&](auto first_stage, auto q0_c, auto q1_c) {
+        constexpr bool kFirst = decltype(first_stage)::value;
+        constexpr int q0 = decltype(q0_c)::value, q1 = decltype(q1_c)::value;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int q = q0; q < q1; ++q) {
+          const int kb = q / MB, mb = q % MB;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.f;
-    }
-    const bool more1 = g + 1 < total;
-    if (young) __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-    for (int q = 0; q < QN - kASlots; ++q) {
-      const int kb = q / MB, mb = q % MB;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb % kBSets][nb], acc[mb][nb]);
-      if constexpr (kTB) {
-        if (q == 0) {
-          read_b(sb, 1);
-          read_b(sb, 2);
-          read_b(sb, 3);
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb % kBSets][nb], (kFirst && kb == 0) ? kZero16 : acc[mb][nb]);
+          if constexpr (kTB) {
+            if (q == 0) {
+              read_b(sb, 1);
+              read_b(sb, 2);
+              read_b(sb, 3);
+            }
+          } else {
+            if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
+          }
+          read_a(sb, q + kASlots);
+          if constexpr (kTB) {
+            if (2 * q < NLOADS) issue_one((g + 1) & 1, 2 * q, more1);
+            if (2 * q + 1 < NLOADS) issue_one((g + 1) & 1, 2 * q + 1, more1);
+          } else {
+            if (q + kASlots < NLOADS) issue_one((g + 1) & 1, q + kASlots, more1);
+          }
         }
-      } else {
-        if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
-      }
-      read_a(sb, q + kASlots);
-      if constexpr (kTB) {
-        if (2 * q < NLOADS) issue_one((g + 1) & 1, 2 * q, more1);
-        if (2 * q + 1 < NLOADS) issue_one((g + 1) & 1, 2 * q + 1, more1);
-      } else {
-        if (q + kASlots < NLOADS) issue_one((g + 1) & 1, q + kASlots, more1);
-      }
-    }
-    // keep that order: each W fragment's matrix instructions, then the reads
-    // its slot (and, at a k-block's start, the idle H set) can take, then a load
 #pragma unroll
-    for (int q = 0; q < QN - kASlots; ++q) {
-      const int kb = q / MB, mb = q % MB;
-      if (kTB && q == 0) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 6 * NB, 0);      // k-blocks 1-3 of B (two reads each)
-        __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
-      } else if (!kTB && mb == 0 && kb + 1 < 4) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);          // next k-block's H fragments
-        __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
-      } else {
+        for (int q = q0; q < q1; ++q) {
+          const int kb = q / MB, mb = q % MB;
+          if (kTB && q == 0) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 6 * NB, 0);      // k-blocks 1-3 of B (two reads each)
+            __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
+          } else if (!kTB && mb == 0 && kb + 1 < 4) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);          // next k-block's H fragments
+            __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one W fragment
+          if (kTB && 2 * q + 1 < NLOADS)
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // two loads
+          else if (kTB ? 2 * q < NLOADS : q + kASlots < NLOADS)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // one load
+        }
+      };
+      typedef std::integral_constant<int, 0> Q0;
+      typedef std::integral_constant<int, MB> QMB;
+      typedef std::integral_constant<int, QN - kASlots> QEnd;
+      main_steps(first_stage, Q0{}, QMB{});
+      main_steps(std::false_type{}, QMB{}, QEnd{});
+      // (after the ordering above: placed before it, this code lands in the
+      // middle of the ordered region and the LDS reads lose their interleaving)
+      issue_done();
+      if (more1) {
+        FLCE_WAIT_VMCNT(0);      // this wave's loads of stage g + 1 have landed in LDS
+        __syncthreads();         // ... and everyone's; every read of stage g is done
+      }
+      if (young) __builtin_amdgcn_s_setprio(1);
+      // the last kASlots steps. In the chunk's last stage there is no barrier
+      // and the loads (zero fill) go to the other buffer, which no wave reads
+      // any more; the fragments read from it there are never used.
+      const bool more2 = g + 2 < total;
+      const int tbuf = more1 ? (g & 1) : ((g + 1) & 1);
+#pragma unroll
+      for (int j = 0; j < kASlots; ++j) {
+        const int q = QN - kASlots + j;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = Mma<T>::step(fa[j], fb[3 % kBSets][nb], acc[q % MB][nb]);
+        if (j == 0) read_b(sn, 0);
+        read_a(sn, j);
+        if constexpr (!kTB) issue_one(tbuf, j, more2);
+      }
+#pragma unroll
+      for (int j = 0; j < kASlots; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
+        if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, (kTB ? 2 * NB : NB) + 1, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (!kTB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);             // one W fragment
-      if (kTB && 2 * q + 1 < NLOADS)
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);           // two loads
-      else if (kTB ? 2 * q < NLOADS : q + kASlots < NLOADS)
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);           // one load
-    }
-    // (after the ordering above: placed before it, this code lands in the
-    // middle of the ordered region and the LDS reads lose their interleaving)
-    issue_done();
-    if (more1) {
-      FLCE_WAIT_VMCNT(0);      // this wave's loads of stage g + 1 have landed in LDS
-      __syncthreads();         // ... and everyone's; every read of stage g is done
-    }
-    if (young) __builtin_amdgcn_s_setprio(1);
-    // the last kASlots steps. In the chunk's last stage there is no barrier
-    // and the loads (zero fill) go to the other buffer, which no wave reads
-    // any more; the fragments read from it there are never used.
-    const bool more2 = g + 2 < total;
-    const int tbuf = more1 ? (g & 1) : ((g + 1) & 1);
-#pragma unroll
-    for (int j = 0; j < kASlots; ++j) {
-      const int q = QN - kASlots + j;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = Mma<T>::step(fa[j], fb[3 % kBSets][nb], acc[q % MB][nb]);
-      if (j == 0) read_b(sn, 0);
-      read_a(sn, j);
-      if constexpr (!kTB) issue_one(tbuf, j, more2);
-    }
-#pragma unroll
-    for (int j = 0; j < kASlots; ++j) {
-      __builtin_amdgcn_sched_group_barrier(0x008, STEPS, 0);
-      if (j == 0) __builtin_amdgcn_sched_group_barrier(0x100, (kTB ? 2 * NB : NB) + 1, 0);
-      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if constexpr (!kTB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-    if (++ks < KS) continue;
-    ks = 0;
+  };
+  for (int g = 0; g < total;) {
+    stage(std::true_type{}, g++);
+    for (int ks = 1; ks < KS; ++ks) stage(std::false_type{}, g++);
 
     const int vw = (tile_begin + tile) * kBV + a_row;   // first A row (vocabulary row) of this wave
     ++tile;
@@ -636,7 +646,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        // target logit: kept by the one lane holding (y, token); written at the end of the chunk
+        // target logit: written by the one lane holding (y, token), in this (rare, divergent) branch
         const int rel = ytok[nb] - vw;
         if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & 1) == (lane >> 5)) {
           int want = rel;
@@ -649,8 +659,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
               if (mb == want_mb && r == want_r) val = acc[mb][nb][r];
-          zt[nb] = val;
-          zhit[nb] = true;
+          p.z_target[t0 + wt * WT + nb * 32 + (lane & 31)] = val;
         }
         // online update: m' = max(m, m_tile), s' = s e^(m - m') + sum_j e^(z_j - m')
         float tmax = kNegInf;
@@ -742,11 +751,6 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 
 
   if constexpr (MODE != kForward) return;
-
-  // ---- target logits found in this chunk
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-    if (zhit[nb]) p.z_target[t0 + wt * WT + nb * 32 + (lane & 31)] = zt[nb];
 
   // ---- end of chunk: combine the two half-waves, then the kWavesV waves that
   // share a token range, in a fixed order (deterministic), and write one
