@@ -333,7 +333,8 @@ def pin_bwd_finite_differences(fwd, bwd):
 
 def pin_bwd_zero_weights(fwd, bwd):
     """W = 0: every row's softmax is uniform, so dH = sum_v dZ_iv W_v = 0 and
-    dW_v = sum_i g_i (1/V - [v == y_i]) H_i."""
+    dW_v = sum_i g_i (1/V - [v == y_i]) H_i; the sizes of dW's terms are
+    |g_i| (1/V + [v == y_i]) |H_i|."""
     rng = np.random.default_rng(41)
     N, D, V = 5, 6, 9
     Hn = rng.standard_normal((N, D)).astype(np.float32)
@@ -342,10 +343,16 @@ def pin_bwd_zero_weights(fwd, bwd):
     out = bwd(_f32(Hn), _f32(np.zeros((V, D))), _y(yn), g)
     _close(out["dH"], np.zeros((N, D)), 0.0, "W=0 dH")
     want = np.zeros((V, D))
+    want_abs = np.zeros((V, D))
     for i in range(N):
         for v in range(V):
-            want[v] += float(g[i]) * ((1.0 / V) - (1.0 if v == yn[i] else 0.0)) * Hn[i].astype(np.float64)
+            hit = 1.0 if v == yn[i] else 0.0
+            want[v] += float(g[i]) * ((1.0 / V) - hit) * Hn[i].astype(np.float64)
+            want_abs[v] += abs(float(g[i])) * ((1.0 / V) + hit) * np.abs(Hn[i].astype(np.float64))
     _close(out["dW"], want, 1e-14, "W=0 dW")
+    # the sizes of the terms: |g_i| (1/V + [v == y_i]) |H_id| summed over i; dH's are all 0
+    _close(out["dW_abs"], want_abs, 1e-14, "W=0 dW_abs")
+    _close(out["dH_abs"], np.zeros((N, D)), 0.0, "W=0 dH_abs")
 
 
 def pin_bwd_single_word(fwd, bwd):
@@ -433,6 +440,86 @@ def pin_bwd_autograd(fwd, bwd):
     _close(out["dW"], Wd.grad.numpy(), 1e-13, "dW vs autograd")
 
 
+# ------------------------------------------------------- sums of |terms| (two-sided)
+# The backward's GPU tolerance is proportional to these sums, so they are
+# pinned from both sides by closed forms: a sum that came out too large would
+# loosen every backward check, one too small would fail correct results.
+def pin_bwd_term_sums_single_word(fwd, bwd):
+    """V = 1: the softmax is 1 and the one-hot is 1, so both terms of dZ_i0
+    have size |g_i|: dH_abs_id = 2 |g_i| |W_0d| and dW_abs_0d = sum_i 2 |g_i| |H_id|
+    (with g, H and W of both signs)."""
+    rng = np.random.default_rng(47)
+    N, D = 5, 9
+    H = _bf16(rng.standard_normal((N, D)))
+    W = _bf16(rng.standard_normal((1, D)))
+    g = np.array([1.25, -0.5, 0.75, -2.0, 0.375], np.float32)
+    out = bwd(H, W, _y([0] * N), g)
+    Hd, Wd, gd = H.double().numpy(), W.double().numpy(), g.astype(np.float64)
+    _close(out["dH_abs"], 2.0 * np.abs(gd)[:, None] * np.abs(Wd[0])[None, :], 1e-15, "V=1 dH_abs")
+    _close(out["dW_abs"], (2.0 * np.abs(gd)[:, None] * np.abs(Hd)).sum(axis=0)[None, :], 1e-14, "V=1 dW_abs")
+
+
+def pin_bwd_term_sums_signed_rows(fwd, bwd):
+    """Vocabulary rows that differ only in the signs of their entries
+    (|W_vd| = |w_d| for every v) give a non-uniform softmax, yet
+    dH_abs_id = |g_i| |w_d| sum_v (p_iv + [v == y_i]) = 2 |g_i| |w_d| for a target
+    in [0, V) (the softmax sums to 1, the one-hot to 1), and |g_i| |w_d| for a
+    target outside [0, V) (an empty one-hot)."""
+    rng = np.random.default_rng(48)
+    N, D, V = 6, 10, 23
+    w = rng.standard_normal(D)
+    W = _bf16(rng.choice([-1.0, 1.0], size=(V, D)) * w[None, :])
+    H = _bf16(rng.standard_normal((N, D)))
+    yn = rng.integers(0, V, N)
+    yn[2] = -1
+    yn[4] = V
+    g = rng.uniform(-1.5, 1.5, N).astype(np.float32)
+    out = bwd(H, W, _y(yn), g)
+    Wd = W.double().numpy()
+    assert np.all(np.abs(Wd) == np.abs(Wd[0])[None, :]), "the rows must share their magnitudes"
+    _, lse, _ = fwd(H, W, _y(yn))
+    z = H.double().numpy() @ Wd.T
+    assert np.ptp(z, axis=1).min() > 1.0, "the softmax must not be uniform"
+    hits = np.where((yn >= 0) & (yn < V), 2.0, 1.0)
+    want = hits[:, None] * np.abs(g.astype(np.float64))[:, None] * np.abs(Wd[0])[None, :]
+    _close(out["dH_abs"], want, 1e-13, "signed rows dH_abs")
+
+
+def pin_bwd_term_sums_columns(fwd, bwd):
+    """For targets in [0, V), sum_v (p_iv + [v == y_i]) = 2 for every row, so each
+    column of dW_abs sums over the vocabulary to 2 sum_i |g_i| |H_id|, whatever
+    the inputs."""
+    rng = np.random.default_rng(49)
+    N, D, V = 7, 12, 40
+    H = _bf16(rng.standard_normal((N, D)))
+    W = _bf16(rng.standard_normal((V, D)) * 0.7)
+    y = _y(rng.integers(0, V, N))
+    g = rng.uniform(-1.0, 2.0, N).astype(np.float32)
+    out = bwd(H, W, y, g)
+    want = 2.0 * (np.abs(g.astype(np.float64))[:, None] * np.abs(H.double().numpy())).sum(axis=0)
+    _close(out["dW_abs"].sum(axis=0), want, 1e-13, "column sums of dW_abs")
+
+
+def pin_bwd_hand_examples(fwd, bwd):
+    """Hand-worked gradients and term sizes stored in
+    tests/golden/hand_examples_backward.json."""
+    with open(os.path.join(GOLDEN, "hand_examples_backward.json")) as f:
+        data = json.load(f)
+    getcontext().prec = 50
+    env = {"ln": lambda x: Decimal(x).ln(), "exp": lambda x: Decimal(x).exp(), "__builtins__": {}}
+
+    def ev(expr):
+        import re
+        return float(eval(re.sub(r"(\d+(?:\.\d+)?)", r"Decimal('\1')", expr), {**env, "Decimal": Decimal}))
+
+    for ex in data["examples"]:
+        for mk in (_bf16, _f32):
+            out = bwd(mk(ex["H"]), mk(ex["W"]), _y(ex["y"]), np.asarray(ex["g"], np.float32))
+            for key in ("dH", "dW", "dH_abs", "dW_abs"):
+                want = [[ev(e) for e in row] for row in ex[key]]
+                _close(out[key], want, 1e-15, f"{ex['name']} {key}")
+
+
 BWD_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_zero_weights,
@@ -441,4 +528,8 @@ BWD_PINS = [
     pin_bwd_out_of_range_target,
     pin_bwd_rows_subset,
     pin_bwd_autograd,
+    pin_bwd_term_sums_single_word,
+    pin_bwd_term_sums_signed_rows,
+    pin_bwd_term_sums_columns,
+    pin_bwd_hand_examples,
 ]

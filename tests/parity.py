@@ -101,7 +101,26 @@ def bwd_bound(abs_sum, dtype, K):
     return (u + 4.0 * np.sqrt(K) * 2.0 ** -24) * np.asarray(abs_sum, dtype=np.float64) + 1e-30
 
 
+# Norm-wise, over all elements of one output: the errors that rounding dZ puts
+# into the terms are u |term| at most and pseudo-random in sign and size (their
+# root mean square is about u / sqrt(6) for round-to-nearest in a binary
+# format), so they add up like the terms themselves when those carry random
+# signs and less when one term dominates: ||error|| is about 0.4 u ||result||,
+# and NORM_C = 1 asserts ||error|| <= u ||result|| (a margin of ~2.5). The
+# error of p (2e-5 relative, the same for a whole row, so it does not average
+# out) and the fp32 sums are bounded by the norm of the sums of |terms| S.
+NORM_C = 1.0
+
+
+def bwd_norm_bound(want, abs_sum, dtype, K):
+    u = UNIT_ROUNDOFF[dtype]
+    return (NORM_C * u * float(np.linalg.norm(want))
+            + (2e-5 + 4.0 * np.sqrt(K) * 2.0 ** -24) * float(np.linalg.norm(abs_sum)) + 1e-30)
+
+
 def check_bwd(got, want, abs_sum, dtype, K, what):
+    """Elementwise (bwd_bound) and norm-wise (bwd_norm_bound) checks of one
+    gradient; returns (max |d|, ||d|| / ||want||)."""
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, f"{what}: shape {got.shape} vs {want.shape}"
@@ -111,7 +130,11 @@ def check_bwd(got, want, abs_sum, dtype, K, what):
         i = int(np.argmax(err - bound))
         raise AssertionError(f"{what}: element {np.unravel_index(i, got.shape)}: got {got.flat[i]!r}, "
                              f"oracle {want.flat[i]!r}, |d|={err.flat[i]:.3e} > {bound.flat[i]:.3e}")
-    rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    del bound
+    enorm = float(np.linalg.norm(err))
+    nb = bwd_norm_bound(want, abs_sum, dtype, K)
+    rel = enorm / max(float(np.linalg.norm(want)), 1e-300)
+    assert enorm <= nb, f"{what}: ||d|| = {enorm:.3e} > {nb:.3e} (relative {rel:.3e})"
     return float(err.max()) if err.size else 0.0, rel
 
 

@@ -200,3 +200,27 @@ def test_backward_stress_shape_sparse_gradient():
                          H.dtype, w.N, f"stress dW rows {v0}..")
         worst = max(worst, e)
     _log(f"[bwd] stress dW max |d| {worst:.3e}")
+
+
+def test_backward_medium_workload_sparse_gradient():
+    """The medium workload (N=4096, D=2048, V=50257, Zipf targets; dH split
+    over the vocabulary) with the upstream gradient on 16 rows, among them
+    rows whose targets are the most frequent word: all of dW (the oracle
+    computes it exactly on those rows alone, the others' dZ being 0) and those
+    rows of dH against the oracle, every other dH row exactly 0."""
+    w = workloads.WORKLOADS["medium_bf16"]
+    _log(f"[bwd] {w.describe()} sparse gradient")
+    H, W, y = workloads.make(w, DEV)
+    yc = y.cpu().numpy()
+    top = np.nonzero(yc == np.bincount(yc).argmax())[0][:4]
+    rows = np.unique(np.concatenate([top, workloads.subset_rows(w.N, 12, seed=31).numpy()]))
+    g = torch.zeros(w.N, dtype=torch.float32)
+    g[torch.as_tensor(rows)] = torch.linspace(-0.75, 1.5, len(rows))
+    g = g.to(DEV)
+    dH, dW = gpu_backward(H, W, y, g)
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    ref = oracle.backward(H.cpu()[sel], W.cpu(), y.cpu()[sel], g.cpu()[sel])
+    eh, rh = check_bwd(dH[rows], ref["dH"], ref["dH_abs"], H.dtype, w.V, "medium dH rows")
+    assert np.all(dH[np.setdiff1d(np.arange(w.N), rows)] == 0.0)
+    ew, rw = check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, w.N, "medium dW")
+    _log(f"[bwd] medium dH max |d| {eh:.3e} rel {rh:.2e}; dW max |d| {ew:.3e} rel {rw:.2e}")

@@ -46,6 +46,15 @@ MUTANTS = {
                              "const double h = widen(H, dtype, (N - 1 - i) * D + d);"),
     "bwd_dW_drop_last_row": ("for (int64_t i = 0; i < N; ++i) {\n          const double h",
                              "for (int64_t i = 0; i < N - 1; ++i) {\n          const double h"),
+    # backward: the sums of |terms| that scale the GPU tolerance (inflated, dropped, signed)
+    "bwd_abs_inflate_hit": ("dzabs[v] = fabs(g[i]) * (p + hit);", "dzabs[v] = fabs(g[i]) * (p + 2.0 * hit);"),
+    "bwd_abs_inflate_p": ("dzabs[v] = fabs(g[i]) * (p + hit);", "dzabs[v] = fabs(g[i]) * (2.0 * p + hit);"),
+    "bwd_abs_drop_hit": ("dzabs[v] = fabs(g[i]) * (p + hit);", "dzabs[v] = fabs(g[i]) * p;"),
+    "bwd_abs_drop_p": ("dzabs[v] = fabs(g[i]) * (p + hit);", "dzabs[v] = fabs(g[i]) * hit;"),
+    "bwd_abs_signed_g": ("dzabs[v] = fabs(g[i]) * (p + hit);", "dzabs[v] = g[i] * (p + hit);"),
+    "bwd_dH_abs_signed_w": ("aabs += dzabs[v] * fabs(w);", "aabs += dzabs[v] * w;"),
+    "bwd_dW_abs_signed_h": ("aabs += dzabs_all[i * V + v] * fabs(h);", "aabs += dzabs_all[i * V + v] * h;"),
+    "bwd_dW_abs_squared_h": ("aabs += dzabs_all[i * V + v] * fabs(h);", "aabs += dzabs_all[i * V + v] * h * h;"),
 }
 
 
