@@ -151,14 +151,18 @@ int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtyp
  *   - dZ is rounded to `dtype` before the two products (fp32 accumulation);
  *     the result differs from exact arithmetic by about the unit roundoff of
  *     `dtype` times the sum of the absolute values of each output's terms.
- *   - The workspace (flce_backward_workspace_bytes, 256-byte aligned,
- *     FLCE_ERR_INVALID_ARG if smaller) holds W and H transposed and dZ of all
- *     rows transposed (V x N elements of `dtype`, each dimension rounded up to
- *     64); for fp32 also dZ of one chunk of rows row-major (chunks keep that
- *     part near 2 GiB at most); for bf16 shapes whose dH product alone would
- *     leave compute units idle, also S x N x D float32 partial sums of dH
- *     (2 <= S <= 16 slices of the vocabulary, added in slice order, so the
- *     result is still deterministic). Allocates nothing.
+ *   - The vocabulary is processed in slices so that dZ, which is N x V, only
+ *     ever exists for one slice: each slice's dZ (transposed; for fp32 also
+ *     row-major) stays within 1 GiB whatever N and V are, each slice writes
+ *     its own rows of dW, and the slices' contributions to dH are added in
+ *     slice order (deterministic). The workspace (flce_backward_workspace_bytes,
+ *     256-byte aligned, FLCE_ERR_INVALID_ARG if smaller) holds one slice of W
+ *     transposed, H transposed and that dZ (each dimension rounded up to 64
+ *     elements); for bf16 shapes whose dH product alone would leave compute
+ *     units idle, also S x N x D float32 partial sums of dH (2 <= S <= 16
+ *     pieces of a slice's contraction, added in order). No O(N x V) memory:
+ *     1.39 GB in all at N = 8192, D = 4096, V = 151936 in bf16, where the
+ *     fp32 logits alone would take 4.98 GB. Allocates nothing.
  *   - Other conventions (alignment, D * sizeof(element) % 16 == 0, stream,
  *     status codes) as for the forward.
  */
@@ -216,14 +220,16 @@ size_t flce_forward_quant_workspace_bytes(int64_t N, int64_t D, int64_t V, int b
  * the one flce_forward_quant defines and lse is its lse_out for the same
  * inputs. The head (codes, scales, biases) gets no gradient. Computed as
  * flce_backward computes dH for the dequantised bf16 W (dZ rounded to bf16,
- * float32 accumulation), one vocabulary slice at a time: the slice's dH
- * contributions are float32 partial products added in slice order at the
- * end (deterministic); a vocabulary that fits one slice gives the same bits
- * as flce_backward's dH on the dequantised W.
+ * float32 accumulation), one vocabulary slice at a time (at most the
+ * forward's dequantisation slice, and small enough that the slice's dZ stays
+ * within 1 GiB): each slice's dH contribution is added into dH in slice order
+ * (deterministic); a vocabulary that fits one slice gives the same bits as
+ * flce_backward's dH on the dequantised W.
  *   - workspace: flce_backward_quant_workspace_bytes(N, D, V, bits, group)
- *     bytes, 256-byte aligned: one dequantised slice, its transpose, dZ of
- *     all rows for the slice (transposed), and the partial products. Allocates
- *     nothing. N == 0 enqueues nothing.
+ *     bytes, 256-byte aligned: one dequantised slice, its transpose and dZ of
+ *     all rows for the slice (transposed); for shapes whose dH product would
+ *     leave compute units idle, also the partial sums of its split
+ *     contraction. Allocates nothing. N == 0 enqueues nothing.
  *   - Format, alignment and status codes as for flce_forward_quant and
  *     flce_backward.
  */

@@ -394,9 +394,11 @@ def linear_cross_entropy_quant(H, codes, scales, biases, targets, bits: int, gro
 class LinearCrossEntropy(torch.autograd.Function):
     """Per-token loss with gradients for H and W: the forward runs flce_forward
     and keeps its lse; the backward hands the incoming per-token gradient to
-    flce_backward, which regenerates the logits tile by tile (the page's
-    training path: the forward's log-sum-exp is kept, the logits are not).
-    The float32 gradients are cast to the inputs' dtype by autograd itself."""
+    flce_backward, which regenerates the logits tile by tile, one vocabulary
+    slice at a time, so dZ never exists beyond one slice (at most 1 GiB): the
+    page's training path keeps the forward's log-sum-exp, not the logits, and
+    runs a chunked backward. The float32 gradients are cast to the inputs'
+    dtype by autograd itself."""
 
     @staticmethod
     def forward(ctx, H, W, targets):

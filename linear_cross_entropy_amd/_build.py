@@ -1,4 +1,5 @@
-"""Compile the HIP library libflce.so in-tree for gfx950."""
+"""Compile the HIP libraries in-tree for gfx950: libflce.so (the fused linear
+cross-entropy) and libflce_ceiling.so (the matrix-core ceiling instrument)."""
 from __future__ import annotations
 
 import os
@@ -9,6 +10,8 @@ ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "flce.hip")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libflce.so")
+CEILING_SRC = os.path.join(PKG, "csrc", "ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libflce_ceiling.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -22,13 +25,21 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+def _compile(src: str, out: str, extra: list[str] | None, verbose: bool) -> str:
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *(extra or []), "-I", INCLUDE, src, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, out)
+    return out
+
+
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Build libflce.so (at `out`) and, beside the default library, the ceiling instrument."""
+    _compile(SRC, out, extra, verbose)
+    if out == LIB:
+        _compile(CEILING_SRC, CEILING_LIB, None, verbose)
     return out
 
 

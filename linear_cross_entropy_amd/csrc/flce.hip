@@ -155,6 +155,8 @@ struct TileArgs {
   // grid, copy s contracting k-stages [s * ks_per, (s + 1) * ks_per) and
   // writing its partial C to C + s * N * ldc
   int ksplit, ks_per;
+  // kGemm and kGemmT: add Z to C instead of overwriting it
+  int accumulate;
 };
 
 // Element-type specific pieces: a 16-byte fragment and the matrix-core step
@@ -423,7 +425,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     ytok[nb] = -1;
     l2tok[nb] = 0.f;
     gtok[nb] = 0.f;
-    if constexpr (MODE != kGemm) {
+    if constexpr (MODE == kForward || MODE == kDz) {
       if (tok < p.N) ytok[nb] = p.y[tok] - p.v_off;
     }
     if constexpr (MODE == kDz) {
@@ -713,8 +715,8 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
           }
       }
     } else if constexpr (MODE == kGemmT) {
-      // ---- C[b][a] = Z for a < V, b < N: four consecutive a per lane and
-      // register group, one 16-byte store each
+      // ---- C[b][a] = Z (or C[b][a] + Z) for a < V, b < N: four consecutive a
+      // per lane and register group, one 16-byte store each
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int b = t0 + wt * WT + nb * 32 + (lane & 31);
@@ -725,13 +727,19 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
           for (int r4 = 0; r4 < 4; ++r4) {
             const int a0 = vw + mb * 32 + 8 * r4 + 4 * (lane >> 5);
             if (a0 >= p.V) continue;
-            const float q[4] = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2],
-                                acc[mb][nb][4 * r4 + 3]};
-            store4((char*)(p.C + ((size_t)kslice * p.N + b) * p.ldc + a0), q);
+            float q[4] = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2],
+                          acc[mb][nb][4 * r4 + 3]};
+            float* dst = p.C + ((size_t)kslice * p.N + b) * p.ldc + a0;
+            if (p.accumulate) {
+              const f32x4 old = *(const f32x4*)dst;
+#pragma unroll
+              for (int j = 0; j < 4; ++j) q[j] = old[j] + q[j];
+            }
+            store4((char*)dst, q);
           }
       }
     } else {
-      // ---- C[a][b] = Z for a < V, b < N
+      // ---- C[a][b] = Z (or C[a][b] + Z) for a < V, b < N
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int b = t0 + wt * WT + nb * 32 + (lane & 31);
@@ -741,7 +749,10 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int a = vw + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            if (a < p.V) p.C[(size_t)a * p.ldc + b] = acc[mb][nb][r];
+            if (a < p.V) {
+              float* dst = p.C + (size_t)a * p.ldc + b;
+              *dst = p.accumulate ? *dst + acc[mb][nb][r] : acc[mb][nb][r];
+            }
           }
       }
     }
@@ -886,12 +897,14 @@ __global__ __launch_bounds__(256) void flce_zero_kernel(float* __restrict__ dst,
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) dst[i] = 0.f;
 }
 
-// Sum of the ksplit partial products of a split dH product, slice by slice
-// in order (so the result does not depend on scheduling). n4 = elements / 4.
+// Sum of the S partial products of a split dH product, in order (so the
+// result does not depend on scheduling), written to out or, with accumulate,
+// added to it. n4 = elements / 4.
 __global__ __launch_bounds__(256) void flce_ksum_kernel(const float* __restrict__ part, int S, int64_t n4,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, int accumulate) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
     f32x4 acc = ((const f32x4*)part)[i];
+    if (accumulate) acc = ((const f32x4*)out)[i] + acc;
     for (int s = 1; s < S; ++s) acc += ((const f32x4*)part)[(int64_t)s * n4 + i];
     ((f32x4*)out)[i] = acc;
   }
@@ -1154,27 +1167,45 @@ int launch_merge(const Plan& pl, const int32_t* y, float* loss, float* lse, cons
 }
 
 // ------------------------------------------------------------------ backward
-// bf16:
-//   1. W^T ([D][Vp]) and H^T ([D][Np]): K-contiguous copies for the products.
-//   2. The dZ pass recomputes Z (the forward's tile loop, full D) for all rows
-//      and writes dZ = g (softmax - onehot) in bf16, transposed: dzt[Vp][Np].
-//   3. dH = dZ . W as C[token][d] with A = W^T and B = dZ read from dzt
-//      through transposing LDS reads (flce_gemmt_kernel): no row-major dZ.
-//   4. dW = dzt . H (A = dzt, B = H^T), contracting over all N rows.
-// fp32 (no transposing reads for 32-bit elements): the dZ pass and the dH
-// product run over chunks of R rows; the dZ pass also writes the chunk's
-// row-major dz[R][Vp], and dH[chunk] = dz . W (A = dz, B = W^T); chunking
-// bounds that row-major dz to about kDzBudget bytes.
-// Vp, Np and the chunk's row count round up to 64 elements, so that the rows
-// of the transposed copies start on 128-byte lines; the padding is written as
-// zeros.
-constexpr double kDzBudget = 2.0 * 1024 * 1024 * 1024;
+// The backward runs the vocabulary in slices of Vs rows, so that dZ only ever
+// exists for one slice. Per slice s (rows [v0, v0 + Vs) of W, Vsp = Vs
+// rounded up to 64):
+//   1. W_s^T ([D][Vsp]), the K-contiguous A operand of dH (transpose kernel);
+//   2. the dZ pass recomputes Z for all rows over the slice's vocabulary (the
+//      forward's tile loop on W rows [v0, v0 + Vs), targets offset by v0) and
+//      writes dZ_s = g (softmax - onehot), rounded to the input dtype,
+//      transposed: dzt[Vsp][Np] (for fp32 also row-major: dz[Np][Vsp]);
+//   3. dH (+)= dZ_s W_s: bf16 reads dZ_s from dzt through transposing LDS
+//      reads (A = W_s^T, B = dzt); fp32 has no transposing 32-bit read and
+//      uses the row-major copy (A = dz, B = W_s^T). The first slice writes dH,
+//      later slices add to it, in slice order (deterministic). When the bf16
+//      product's tiles would leave compute units idle, its contraction is
+//      split again into float32 partial sums that flce_ksum_kernel adds in
+//      order;
+//   4. dW[v0, v0 + Vs) = dzt . H (A = dzt, B = H^T [D][Np], transposed once
+//      per call): each slice owns its rows of dW, nothing is accumulated.
+// Vs is the largest size (balanced over the slices) whose dZ buffers fit
+// kDzBudget bytes, one transposed copy for bf16 and two copies for fp32, so
+// the workspace is W_s^T + H^T + at most kDzBudget of dZ (+ the bf16 split's
+// partial sums at shapes too small to fill the chip): it grows with V D and
+// N D, never with N V. Padding rows and columns (to 64 elements, so that rows
+// of the transposed copies start on 128-byte lines) are written as zeros, so
+// the products need no masks on K.
+constexpr double kDzBudget = 1024.0 * 1024 * 1024;
+
+// The launches of one vocabulary slice of Vs rows.
+struct SlicePlans {
+  int64_t Vs, Vsp;
+  Plan dz, dh, dw;     // dZ pass; dH product; dW product (dw unused when dW is not wanted)
+  int ksplit, ks_per;  // bf16 dH: K slices and k-stages per slice
+};
 
 struct BwdPlan {
-  int64_t N, D, V, Vp, Np, R, Rp;
-  int dtype, chunks;
-  int ksplit, ks_per;  // bf16 dH: K slices and k-stages per slice
-  size_t es, off_wt, off_ht, off_dz, off_dzt, off_part, ws_bytes;
+  int64_t N, D, V, Np, Vs;  // Vs: rows of every slice but the last
+  int dtype, slices;
+  size_t es;
+  SlicePlans full, last;
+  size_t off_wt, off_ht, off_dzt, off_dz, off_part, ws_bytes;
 };
 
 // K slices for the transposed-B dH product: when its tiles leave CUs idle,
@@ -1192,6 +1223,37 @@ void gemmt_split(const Plan& ph, int* ksplit, int* ks_per) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Plans of one slice's launches (N > 0). with_dw: plan the dW product too.
+int make_slice_plans(int64_t N, int64_t D, int64_t Vs, int64_t Np, int dtype, bool with_dw, SlicePlans* sp) {
+  sp->Vs = Vs;
+  sp->Vsp = round_up(Vs, 64);
+  sp->ksplit = 1;
+  sp->ks_per = 0;
+  int rc;
+  if ((rc = make_plan(N, D, Vs, dtype, &sp->dz)) != FLCE_OK) return rc;                     // dZ
+  if (dtype == FLCE_BF16) {
+    if ((rc = make_plan(N, sp->Vsp, D, dtype, &sp->dh, kTile320)) != FLCE_OK) return rc;    // dH (transposed B)
+    gemmt_split(sp->dh, &sp->ksplit, &sp->ks_per);
+  } else {
+    if ((rc = make_plan(D, sp->Vsp, N, dtype, &sp->dh)) != FLCE_OK) return rc;              // dH
+  }
+  if (with_dw && (rc = make_plan(D, Np, Vs, dtype, &sp->dw)) != FLCE_OK) return rc;        // dW
+  return FLCE_OK;
+}
+
+// Vocabulary rows per slice: every slice's dZ (dz_copies copies of Vsp x Np
+// elements) fits kDzBudget bytes, the slices are balanced, and a slice is a
+// multiple of 3840 rows (whole 256-, 320- and 384-row tiles) when that
+// leaves at least one such block, else of 64.
+int64_t slice_rows(int64_t V, int64_t Np, int64_t es, int dz_copies) {
+  const int64_t cap = (int64_t)(kDzBudget / ((double)Np * (double)es * dz_copies));
+  const int64_t gran = cap >= 3840 ? 3840 : 64;
+  const int64_t maxv = std::max<int64_t>(cap / gran * gran, 64);
+  if (V <= maxv) return V;
+  const int64_t n = (V + maxv - 1) / maxv;
+  return std::min(maxv, round_up((V + n - 1) / n, gran));
+}
+
 int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
   if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
   if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
@@ -1203,47 +1265,30 @@ int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
   bp->V = V;
   bp->dtype = dtype;
   bp->es = (size_t)es;
-  bp->Vp = round_up(V, 64);
   bp->Np = round_up(N, 64);
-  if (dtype == FLCE_BF16) {
-    // one pass over all rows, no row-major dZ; a stage of the transposed B
-    // (64 k-rows of dzt) stays under 2^31 bytes
-    if (bp->Np * 2 * 64 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
-    bp->R = N;
-    bp->chunks = N > 0 ? 1 : 0;
-  } else if (N > 0) {
-    const double per_row = (double)bp->Vp * (double)es;
-    int64_t nc = (int64_t)((double)N * per_row / kDzBudget) + 1;
-    if (nc > N) nc = N;
-    bp->R = std::min(round_up((N + nc - 1) / nc, 256), bp->Np);
-    bp->chunks = (int)((N + bp->R - 1) / bp->R);
-  } else {
-    bp->R = 0;
-    bp->chunks = 0;
-  }
-  bp->Rp = round_up(bp->R, 8);
-  bp->ksplit = 1;
-  bp->ks_per = 0;
-  // every pass must plan (32-bit offsets, resource sizes)
-  Plan pl;
+  // a stage of the transposed B (64 k-rows of dzt) stays under 2^31 bytes
+  if (bp->Np * es * 64 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  bp->Vs = slice_rows(V, bp->Np, es, dtype == FLCE_BF16 ? 1 : 2);
+  bp->slices = N > 0 ? (int)((V + bp->Vs - 1) / bp->Vs) : 0;
   int rc;
-  if (bp->R > 0) {
-    if ((rc = make_plan(bp->R, D, V, dtype, &pl)) != FLCE_OK) return rc;          // dZ
-    if (dtype == FLCE_BF16) {
-      if ((rc = make_plan(N, bp->Vp, D, dtype, &pl, kTile320)) != FLCE_OK) return rc;  // dH (transposed B)
-      gemmt_split(pl, &bp->ksplit, &bp->ks_per);
-    } else {
-      if ((rc = make_plan(D, bp->Vp, bp->R, dtype, &pl)) != FLCE_OK) return rc;   // dH
-    }
-    if ((rc = make_plan(D, bp->Np, V, dtype, &pl)) != FLCE_OK) return rc;         // dW
+  if (N > 0) {
+    if ((rc = make_slice_plans(N, D, bp->Vs, bp->Np, dtype, true, &bp->full)) != FLCE_OK) return rc;
+    if ((rc = make_slice_plans(N, D, V - (int64_t)(bp->slices - 1) * bp->Vs, bp->Np, dtype, true, &bp->last)) !=
+        FLCE_OK)
+      return rc;
+  } else {
+    bp->full.Vsp = bp->last.Vsp = 0;
+    bp->full.ksplit = bp->last.ksplit = 1;
   }
-  if (bp->Vp * es >= (int64_t(1) << 31) || bp->Np * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  const int64_t vsp = bp->full.Vsp;
+  if (vsp * es >= (int64_t(1) << 31) || bp->Np * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  const int parts = std::max(bp->full.ksplit, bp->last.ksplit);
   bp->off_wt = 0;
-  bp->off_ht = align_up((size_t)(D * bp->Vp * es));
-  bp->off_dz = bp->off_ht + align_up((size_t)(D * bp->Np * es));
-  bp->off_dzt = bp->off_dz + (dtype == FLCE_BF16 ? 0 : align_up((size_t)(bp->Rp * bp->Vp * es)));
-  bp->off_part = bp->off_dzt + align_up((size_t)(bp->Vp * bp->Np * es));
-  bp->ws_bytes = bp->off_part + (bp->ksplit > 1 ? align_up((size_t)bp->ksplit * (size_t)(N * D) * 4) : 0);
+  bp->off_ht = align_up((size_t)(D * vsp * es));
+  bp->off_dzt = bp->off_ht + align_up((size_t)(D * bp->Np * es));
+  bp->off_dz = bp->off_dzt + align_up((size_t)(vsp * bp->Np * es));
+  bp->off_part = bp->off_dz + (dtype == FLCE_BF16 ? 0 : align_up((size_t)(bp->Np * vsp * es)));
+  bp->ws_bytes = bp->off_part + (parts > 1 ? align_up((size_t)parts * (size_t)(N * D) * 4) : 0);
   return FLCE_OK;
 }
 
@@ -1255,94 +1300,95 @@ void launch_transpose(const void* in, int rows, int cols, int64_t ld_in, void* o
                      (T*)out, ld_out, out_len);
 }
 
+void launch_ksum(const float* part, int S, int64_t n, float* out, bool accumulate, hipStream_t stream) {
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(flce_ksum_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 2048)), dim3(256), 0,
+                     stream, part, S, n4, out, accumulate ? 1 : 0);
+}
+
+// Buffers of a backward call, in the workspace.
+struct BwdBuffers {
+  char* wt;     // W_s^T [D][Vsp]
+  char* ht;     // H^T [D][Np] (only when dW is wanted)
+  char* dzt;    // dZ_s^T [Vsp][Np]
+  char* dz;     // dZ_s [Np][Vsp] (fp32 only)
+  float* part;  // bf16 split dH partial sums
+};
+
+// Steps 1-4 for one slice: Ws = W rows [v0, v0 + Vs); dH is written
+// (first) or added to; dWs (rows [v0, v0 + Vs) of dW) is written when not null.
+void backward_slice(const SlicePlans& sp, int dtype, int64_t N, int64_t D, int64_t Np, const void* H,
+                    const void* Ws, int64_t v0, const int32_t* y, const float* lse, const float* grad, float* dH,
+                    bool first, float* dWs, const BwdBuffers& b, hipStream_t stream) {
+  const bool bf = dtype == FLCE_BF16;
+  if (bf)
+    launch_transpose<__bf16>(Ws, (int)sp.Vs, (int)D, D, b.wt, sp.Vsp, (int)sp.Vsp, stream);
+  else
+    launch_transpose<float>(Ws, (int)sp.Vs, (int)D, D, b.wt, sp.Vsp, (int)sp.Vsp, stream);
+  // dZ of the slice: dzt columns [0, Np) and rows [0, Vsp) (padding as zeros)
+  TileArgs a = tile_args(sp.dz, H, Ws);
+  a.y = y;
+  a.v_off = (int)v0;
+  a.lse = lse;
+  a.grad = grad;
+  a.dz = bf ? nullptr : b.dz;
+  a.dzt = b.dzt;
+  a.dz_ld = (int)sp.Vsp;
+  a.dzt_ld = (int)Np;
+  a.dz_rows = (int)Np;
+  a.dz_cols = (int)sp.Vsp;
+  FLCE_LAUNCH_TILES(flce_dz_kernel, sp.dz, a, stream);
+  if (bf) {
+    // dH[token][d] (+)= sum_v dZ[token][v] W_s[v][d]: A = W_s^T, B = dZ read from dzt
+    TileArgs g = tile_args(sp.dh, b.dzt, b.wt);
+    g.ldb = (int)Np;
+    g.ldc = (int)D;
+    g.ksplit = sp.ksplit;
+    g.ks_per = sp.ks_per;
+    g.C = sp.ksplit > 1 ? b.part : dH;
+    g.accumulate = (sp.ksplit == 1 && !first) ? 1 : 0;
+    Plan phs = sp.dh;
+    phs.grid = sp.dh.row_blocks * sp.dh.chunks * sp.ksplit;
+    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, phs, g, stream);
+    if (sp.ksplit > 1) launch_ksum(b.part, sp.ksplit, N * D, dH, !first, stream);
+  } else {
+    // dH[token][d] (+)= sum_v dz[token][v] W_s^T[d][v]: A = dz, B = W_s^T
+    TileArgs g = tile_args(sp.dh, b.wt, b.dz);
+    g.C = dH;
+    g.ldc = (int)D;
+    g.accumulate = first ? 0 : 1;
+    FLCE_LAUNCH_TILES(flce_gemm_kernel, sp.dh, g, stream);
+  }
+  if (dWs) {
+    // dW_s[v][d] = sum_token dzt[v][token] H^T[d][token]: A = dzt, B = H^T
+    TileArgs w = tile_args(sp.dw, b.ht, b.dzt);
+    w.C = dWs;
+    w.ldc = (int)D;
+    FLCE_LAUNCH_TILES(flce_gemm_kernel, sp.dw, w, stream);
+  }
+}
+
 int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32_t* y, const float* lse,
                     const float* grad, float* dH, float* dW, void* ws, hipStream_t stream) {
-  if (bp.chunks == 0) {  // no rows: dW = 0
+  if (bp.slices == 0) {  // no rows: dW = 0
     const int64_t n = bp.V * bp.D;
     hipLaunchKernelGGL(flce_zero_kernel, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 4096)), dim3(256), 0,
                        stream, dW, n);
     return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
   char* base = (char*)ws;
-  char* wt = base + bp.off_wt;
-  char* ht = base + bp.off_ht;
-  char* dz = base + bp.off_dz;
-  char* dzt = base + bp.off_dzt;
-  const bool bf = bp.dtype == FLCE_BF16;
-  // W^T: [D][Vp] and H^T: [D][Np]
-  if (bf) {
-    launch_transpose<__bf16>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
-    launch_transpose<__bf16>(H, (int)bp.N, (int)bp.D, bp.D, ht, bp.Np, (int)bp.Np, stream);
-  } else {
-    launch_transpose<float>(W, (int)bp.V, (int)bp.D, bp.D, wt, bp.Vp, (int)bp.Vp, stream);
-    launch_transpose<float>(H, (int)bp.N, (int)bp.D, bp.D, ht, bp.Np, (int)bp.Np, stream);
+  const BwdBuffers b = {base + bp.off_wt, base + bp.off_ht, base + bp.off_dzt, base + bp.off_dz,
+                        (float*)(base + bp.off_part)};
+  if (bp.dtype == FLCE_BF16)
+    launch_transpose<__bf16>(H, (int)bp.N, (int)bp.D, bp.D, b.ht, bp.Np, (int)bp.Np, stream);
+  else
+    launch_transpose<float>(H, (int)bp.N, (int)bp.D, bp.D, b.ht, bp.Np, (int)bp.Np, stream);
+  for (int s = 0; s < bp.slices; ++s) {
+    const SlicePlans& sp = s + 1 < bp.slices ? bp.full : bp.last;
+    const int64_t v0 = (int64_t)s * bp.Vs;
+    backward_slice(sp, bp.dtype, bp.N, bp.D, bp.Np, H, (const char*)W + v0 * bp.D * (int64_t)bp.es, v0, y, lse,
+                   grad, dH, s == 0, dW + v0 * bp.D, b, stream);
   }
-  if (bf) {
-    // dZ of all rows, transposed only
-    Plan pz, ph;
-    if (make_plan(bp.N, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK ||
-        make_plan(bp.N, bp.Vp, bp.D, bp.dtype, &ph, kTile320) != FLCE_OK)
-      return FLCE_ERR_UNSUPPORTED;
-    TileArgs a = tile_args(pz, H, W);
-    a.y = y;
-    a.lse = lse;
-    a.grad = grad;
-    a.dz = nullptr;
-    a.dzt = dzt;
-    a.dzt_ld = (int)bp.Np;
-    a.dz_rows = (int)bp.Np;
-    a.dz_cols = (int)bp.Vp;
-    FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
-    // dH[token][d] = sum_v dZ[token][v] W[v][d]: A = W^T [D][Vp], B = dZ read from dzt [Vp][Np]
-    TileArgs g = tile_args(ph, dzt, wt);
-    g.ldb = (int)bp.Np;
-    g.ldc = (int)bp.D;
-    g.ksplit = bp.ksplit;
-    g.ks_per = bp.ks_per;
-    float* part = (float*)(base + bp.off_part);
-    g.C = bp.ksplit > 1 ? part : dH;
-    Plan phs = ph;
-    phs.grid = ph.row_blocks * ph.chunks * bp.ksplit;
-    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, phs, g, stream);
-    if (bp.ksplit > 1) {
-      const int64_t n4 = bp.N * bp.D / 4;
-      hipLaunchKernelGGL(flce_ksum_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 2048)), dim3(256), 0,
-                         stream, (const float*)part, bp.ksplit, n4, dH);
-    }
-  }
-  for (int c = 0; c < (bf ? 0 : bp.chunks); ++c) {
-    const int64_t r0 = (int64_t)c * bp.R;
-    const int64_t rc = std::min(bp.R, bp.N - r0);
-    const int64_t rcp = std::min(round_up(rc, 64), bp.Np - r0);
-    const char* Hc = (const char*)H + r0 * bp.D * (int64_t)bp.es;
-    Plan pz, ph;
-    if (make_plan(rc, bp.D, bp.V, bp.dtype, &pz) != FLCE_OK || make_plan(bp.D, bp.Vp, rc, bp.dtype, &ph) != FLCE_OK)
-      return FLCE_ERR_UNSUPPORTED;
-    // dZ of the chunk: rows [0, rcp) of dz, columns [r0, r0 + rcp) of dzt
-    TileArgs a = tile_args(pz, Hc, W);
-    a.y = y + r0;
-    a.lse = lse + r0;
-    a.grad = grad + r0;
-    a.dz = dz;
-    a.dzt = dzt + r0 * (int64_t)bp.es;
-    a.dz_ld = (int)bp.Vp;
-    a.dzt_ld = (int)bp.Np;
-    a.dz_rows = (int)rcp;
-    a.dz_cols = (int)bp.Vp;
-    FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
-    // dH[chunk] = dz . W: A = dz [rc][Vp], B = W^T [D][Vp]
-    TileArgs g = tile_args(ph, wt, dz);
-    g.C = dH + r0 * bp.D;
-    g.ldc = (int)bp.D;
-    FLCE_LAUNCH_TILES(flce_gemm_kernel, ph, g, stream);
-  }
-  // dW = dzt . H: A = dzt [V][Np], B = H^T [D][Np]
-  Plan pw;
-  if (make_plan(bp.D, bp.Np, bp.V, bp.dtype, &pw) != FLCE_OK) return FLCE_ERR_UNSUPPORTED;
-  TileArgs w = tile_args(pw, ht, dzt);
-  w.C = dW;
-  w.ldc = (int)bp.D;
-  FLCE_LAUNCH_TILES(flce_gemm_kernel, pw, w, stream);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
@@ -1432,31 +1478,41 @@ int launch_forward_quant(const QuantPlan& qp, const void* H, const uint8_t* code
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
-// Backward of the quantised-head forward for a frozen head: dH only. Per
-// vocabulary slice, as in the forward: dequantise, transpose the slice (the
-// dH product's A operand), the dZ pass over all rows for the slice's
-// vocabulary (targets offset by its first row), and the transposed-B dH
-// product over the slice's vocabulary, written as partial products (one per
-// slice, times its own K split); flce_ksum_kernel adds them in slice order.
+// Backward of the quantised-head forward for a frozen head: dH only. The
+// vocabulary runs in slices as in the dense backward (backward_slice without
+// dW), each first dequantised into the workspace; a slice is at most the
+// forward's dequantisation slice and keeps dZ^T within kDzBudget.
 struct QuantBwdPlan {
-  QuantPlan q;           // slices and Vs
-  BwdPlan full, last;    // Vp, Np, K split of a full slice and of the last one
-  int parts;             // partial dH products over all slices
+  int64_t N, D, V, Np, Vs;
+  int bits, group, slices;
+  SlicePlans full, last;
   size_t off_w, off_wt, off_dzt, off_part, ws_bytes;
 };
 
 int make_quant_bwd_plan(int64_t N, int64_t D, int64_t V, int bits, int group, QuantBwdPlan* qb) {
   int rc;
-  if ((rc = make_quant_plan(N, D, V, bits, group, &qb->q)) != FLCE_OK) return rc;
-  const int64_t v_last = V - (int64_t)(qb->q.slices - 1) * qb->q.Vs;
-  if ((rc = make_bwd_plan(N, D, qb->q.Vs, FLCE_BF16, &qb->full)) != FLCE_OK) return rc;
-  if ((rc = make_bwd_plan(N, D, v_last, FLCE_BF16, &qb->last)) != FLCE_OK) return rc;
-  qb->parts = (qb->q.slices - 1) * qb->full.ksplit + qb->last.ksplit;
+  QuantPlan q;
+  if ((rc = make_quant_plan(N, D, V, bits, group, &q)) != FLCE_OK) return rc;
+  qb->N = N;
+  qb->D = D;
+  qb->V = V;
+  qb->bits = bits;
+  qb->group = group;
+  qb->Np = round_up(N, 64);
+  if (qb->Np * 2 * 64 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
+  qb->Vs = std::min(q.Vs, slice_rows(V, qb->Np, 2, 1));
+  qb->slices = (int)((V + qb->Vs - 1) / qb->Vs);
+  if ((rc = make_slice_plans(N, D, qb->Vs, qb->Np, FLCE_BF16, false, &qb->full)) != FLCE_OK) return rc;
+  if ((rc = make_slice_plans(N, D, V - (int64_t)(qb->slices - 1) * qb->Vs, qb->Np, FLCE_BF16, false, &qb->last)) !=
+      FLCE_OK)
+    return rc;
+  const int64_t vsp = qb->full.Vsp;
+  const int parts = std::max(qb->full.ksplit, qb->last.ksplit);
   qb->off_w = 0;
-  qb->off_wt = align_up((size_t)(qb->q.Vs * D * 2));
-  qb->off_dzt = qb->off_wt + align_up((size_t)(D * qb->full.Vp * 2));
-  qb->off_part = qb->off_dzt + align_up((size_t)(qb->full.Vp * qb->full.Np * 2));
-  qb->ws_bytes = qb->off_part + (qb->parts > 1 ? align_up((size_t)qb->parts * (size_t)(N * D) * 4) : 0);
+  qb->off_wt = align_up((size_t)(qb->Vs * D * 2));
+  qb->off_dzt = qb->off_wt + align_up((size_t)(D * vsp * 2));
+  qb->off_part = qb->off_dzt + align_up((size_t)(vsp * qb->Np * 2));
+  qb->ws_bytes = qb->off_part + (parts > 1 ? align_up((size_t)parts * (size_t)(N * D) * 4) : 0);
   return FLCE_OK;
 }
 
@@ -1465,49 +1521,15 @@ int launch_backward_quant(const QuantBwdPlan& qb, const void* H, const uint8_t* 
                           void* ws, hipStream_t stream) {
   char* base = (char*)ws;
   __bf16* wbuf = (__bf16*)(base + qb.off_w);
-  char* wt = base + qb.off_wt;
-  char* dzt = base + qb.off_dzt;
-  float* part = (float*)(base + qb.off_part);
-  const QuantPlan& q = qb.q;
-  const size_t code_row = (size_t)(q.bits == 8 ? q.D : q.D / 2);
-  const int64_t groups = q.D / q.group;
-  int64_t p0 = 0;
-  for (int k = 0; k < q.slices; ++k) {
-    const BwdPlan& bp = k + 1 < q.slices ? qb.full : qb.last;
-    const int64_t v0 = (int64_t)k * q.Vs;
-    launch_dequant(q.bits, (int)q.D, q.group, codes + v0 * code_row, scales + v0 * groups, biases + v0 * groups,
-                   bp.V, wbuf, stream);
-    launch_transpose<__bf16>(wbuf, (int)bp.V, (int)q.D, q.D, wt, bp.Vp, (int)bp.Vp, stream);
-    Plan pz, ph;
-    if (make_plan(q.N, q.D, bp.V, FLCE_BF16, &pz) != FLCE_OK ||
-        make_plan(q.N, bp.Vp, q.D, FLCE_BF16, &ph, kTile320) != FLCE_OK)
-      return FLCE_ERR_UNSUPPORTED;
-    TileArgs a = tile_args(pz, H, wbuf);
-    a.y = y;
-    a.v_off = (int)v0;
-    a.lse = lse;
-    a.grad = grad;
-    a.dz = nullptr;
-    a.dzt = dzt;
-    a.dzt_ld = (int)bp.Np;
-    a.dz_rows = (int)bp.Np;
-    a.dz_cols = (int)bp.Vp;
-    FLCE_LAUNCH_TILES(flce_dz_kernel, pz, a, stream);
-    TileArgs g = tile_args(ph, dzt, wt);
-    g.ldb = (int)bp.Np;
-    g.ldc = (int)q.D;
-    g.ksplit = bp.ksplit;
-    g.ks_per = bp.ks_per;
-    g.C = qb.parts > 1 ? part + (size_t)p0 * (size_t)(q.N * q.D) : dH;
-    Plan phs = ph;
-    phs.grid = ph.row_blocks * ph.chunks * bp.ksplit;
-    FLCE_LAUNCH_TILES_GEMMT(flce_gemmt_kernel, phs, g, stream);
-    p0 += bp.ksplit;
-  }
-  if (qb.parts > 1) {
-    const int64_t n4 = q.N * q.D / 4;
-    hipLaunchKernelGGL(flce_ksum_kernel, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 2048)), dim3(256), 0,
-                       stream, (const float*)part, qb.parts, n4, dH);
+  const BwdBuffers b = {base + qb.off_wt, nullptr, base + qb.off_dzt, nullptr, (float*)(base + qb.off_part)};
+  const size_t code_row = (size_t)(qb.bits == 8 ? qb.D : qb.D / 2);
+  const int64_t groups = qb.D / qb.group;
+  for (int k = 0; k < qb.slices; ++k) {
+    const SlicePlans& sp = k + 1 < qb.slices ? qb.full : qb.last;
+    const int64_t v0 = (int64_t)k * qb.Vs;
+    launch_dequant(qb.bits, (int)qb.D, qb.group, codes + v0 * code_row, scales + v0 * groups, biases + v0 * groups,
+                   sp.Vs, wbuf, stream);
+    backward_slice(sp, FLCE_BF16, qb.N, qb.D, qb.Np, H, wbuf, v0, y, lse, grad, dH, k == 0, nullptr, b, stream);
   }
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }

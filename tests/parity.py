@@ -133,7 +133,8 @@ def check_bwd(got, want, abs_sum, dtype, K, what):
     del bound
     enorm = float(np.linalg.norm(err))
     nb = bwd_norm_bound(want, abs_sum, dtype, K)
-    rel = enorm / max(float(np.linalg.norm(want)), 1e-300)
+    wnorm = float(np.linalg.norm(want))
+    rel = enorm / wnorm if wnorm > 0 else float("nan")
     assert enorm <= nb, f"{what}: ||d|| = {enorm:.3e} > {nb:.3e} (relative {rel:.3e})"
     return float(err.max()) if err.size else 0.0, rel
 

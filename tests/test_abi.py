@@ -162,38 +162,75 @@ def test_backward_arguments_rejected_before_any_launch(flce):
     assert bwd(nb=need - 1) == flce.FLCE_ERR_INVALID_ARG
 
 
-def test_backward_workspace_layout(flce):
-    """The workspace holds W^T, H^T and dZ^T of all rows, each rounded to 64
-    elements and 256-byte aligned; fp32 also holds one chunk of row-major dZ,
-    chunks keeping it near 2 GiB (bf16 reads dZ^T transposed instead)."""
-    def up(x, m):
-        return (x + m - 1) // m * m
+DZ_BUDGET = 2 ** 30   # bytes of dZ (one slice of the vocabulary) a backward call holds at once
 
+
+def _up(x, m):
+    return (x + m - 1) // m * m
+
+
+def _slice_rows(N, V, es, copies):
+    """Vocabulary rows per slice: the largest balanced size whose dZ buffers
+    (copies x Vsp x Np elements) fit the budget, in multiples of 3840 rows (or
+    64 when the budget holds fewer)."""
+    Np = _up(N, 64)
+    cap = DZ_BUDGET // (Np * es * copies)
+    gran = 3840 if cap >= 3840 else 64
+    maxv = max(cap // gran * gran, 64)
+    if V <= maxv:
+        return V
+    n = -(-V // maxv)
+    return min(maxv, _up(-(-V // n), gran))
+
+
+def test_backward_workspace_layout(flce):
+    """The workspace holds W_s^T for one vocabulary slice, H^T, and dZ^T of
+    that slice (for fp32 also its row-major dZ), each rounded to 64 elements
+    and 256-byte aligned; where the bf16 dH product is split over the
+    vocabulary, S partial N x D float32 sums."""
     splits = {}
     for N, D, V, dt, es in [(4, 8, 10, 0, 2), (128, 64, 1024, 1, 4), (8192, 4096, 151936, 0, 2),
                             (2048, 1024, 32000, 0, 2), (4096, 2048, 50257, 0, 2),
                             (5000, 64, 262144, 0, 2), (0, 8, 10, 0, 2), (5000, 64, 262144, 1, 4),
-                            (0, 8, 10, 1, 4)]:
-        Vp, Np = up(V, 64), up(N, 64)
-        if N and dt == 1:
-            nc = int(N * Vp * es / 2 ** 31) + 1
-            R = min(up(-(-N // nc), 256), Np)
-        else:
-            R = 0
-        Rp = up(R, 8)
-        want = (up(D * Vp * es, 256) + up(D * Np * es, 256) + up(Rp * Vp * es, 256) + up(Vp * Np * es, 256))
+                            (0, 8, 10, 1, 4), (8192, 8192, 262144, 0, 2), (8192, 4096, 151936, 1, 4)]:
+        Np = _up(N, 64)
+        Vs = _slice_rows(N, V, es, 2 if dt == 1 else 1) if N else 0
+        Vsp = _up(Vs, 64)
+        want = (_up(D * Vsp * es, 256) + _up(D * Np * es, 256) + _up(Vsp * Np * es, 256)
+                + (_up(Np * Vsp * es, 256) if dt == 1 else 0))
         got = flce.flce_backward_workspace_bytes(N, D, V, dt)
-        # plus, where the bf16 dH product is split over the vocabulary, S partial N x D float32 sums
-        S = [s for s in range(1, 17) if got == want + (up(s * N * D * 4, 256) if s > 1 else 0)]
+        S = [s for s in range(1, 17) if got == want + (_up(s * N * D * 4, 256) if s > 1 else 0)]
         assert S, (N, D, V, dt, got, want)
         assert S[0] == 1 or (dt == 0 and N > 0), (N, D, V, dt)
         splits[(N, D, V, dt)] = S[0]
-        if N and dt == 1:
-            assert Rp * Vp * es <= 2 ** 31 + 256 * Vp * es    # one chunk of dZ stays near the budget
     assert splits[(8192, 4096, 151936, 0)] == 1       # enough dH tiles to fill the chip alone
     assert splits[(2048, 1024, 32000, 0)] > 1        # 32 dH tiles: split over the vocabulary
     assert splits[(4, 8, 10, 0)] == 1                # too little K to split
     assert flce.flce_backward_workspace_bytes(4, 12, 10, 0) == 0   # unsupported D
+    # the slicing itself: the production shape takes three slices, the stress shape five;
+    # the GPU test of ragged rows and slices relies on 88320 (bf16) and 23040 (fp32)
+    assert _slice_rows(8192, 151936, 2, 1) == 53760
+    assert -(-262144 // _slice_rows(8192, 262144, 2, 1)) == 5
+    assert _slice_rows(5000, 262144, 2, 1) == 88320 and _slice_rows(5000, 262144, 4, 2) == 23040
+
+
+@pytest.mark.parametrize("N,D,V", [(8192, 4096, 151936), (8192, 8192, 262144), (65536, 4096, 151936),
+                                   (262144, 4096, 151936), (5000, 64, 262144)])
+@pytest.mark.parametrize("dt", [0, 1])
+def test_backward_memory_is_bounded(flce, N, D, V, dt):
+    """No O(N V) memory: the dZ the backward holds at once stays within the
+    1 GiB budget whatever N and V are, so the workspace is at most one slice of
+    W^T, H^T and the budget (the N x V fp32 logits of the production shape
+    alone would be 4.98 GB)."""
+    es = 2 if dt == 0 else 4
+    Np = _up(N, 64)
+    Vs = _slice_rows(N, V, es, 2 if dt == 1 else 1)
+    Vsp = _up(Vs, 64)
+    dz_bytes = Vsp * Np * es * (2 if dt == 1 else 1)
+    assert dz_bytes <= DZ_BUDGET
+    got = flce.flce_backward_workspace_bytes(N, D, V, dt)
+    assert 0 < got <= D * Vsp * es + D * Np * es + DZ_BUDGET + 4 * 256
+    assert got < 0.4 * N * V * 4
 
 
 def test_python_binding_validates_shapes(flce):
@@ -270,13 +307,20 @@ def test_quant_backward_arguments_rejected_before_any_launch(flce):
     assert qb(nb=need - 1) == flce.FLCE_ERR_INVALID_ARG
     assert qb(N=0) == flce.FLCE_OK
     assert flce.flce_backward_quant_workspace_bytes(0, 64, 100, 8, 32) == 0
-    # one slice, its transpose, dZ^T of the slice, and (when there is more than one) the partial dH products
+    # one dequantised slice, its transpose and dZ^T of the slice; the slices add
+    # their dH products into dH in place, so no per-slice partial sums
     up = lambda x, m=256: (x + m - 1) // m * m
     N, D, V = 8192, 4096, 151936
     vs, Np = 30720, 8192
     base = up(vs * D * 2) + up(D * vs * 2) + up(vs * Np * 2)
     got = flce.flce_backward_quant_workspace_bytes(N, D, V, 4, 64)
-    assert got == base + up(5 * N * D * 4)                 # five slices, no split within a slice
+    assert got == base                                     # five slices, no split within a slice
+    # with many rows the slice shrinks so that its dZ^T stays within the budget
+    N = 65536
+    vs = _slice_rows(N, V, 2, 1)
+    assert vs < 30720 and vs * N * 2 <= DZ_BUDGET
+    got = flce.flce_backward_quant_workspace_bytes(N, D, V, 4, 64)
+    assert got == up(vs * D * 2) + up(D * vs * 2) + up(vs * N * 2)
 
 
 def test_header_is_plain_c_and_links(flce, tmp_path):

@@ -156,17 +156,23 @@ def test_backward_vocabulary_split_workloads(name):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_backward_ragged_rows_and_row_chunks(dtype):
+def test_backward_ragged_rows_and_vocabulary_slices(dtype):
     """N=5000, V=262144 with the upstream gradient on a few rows (the others
-    must get dH = 0). bf16 runs one pass over all rows and reads dZ^T
-    transposed for dH; fp32 runs three row chunks of the row-major dZ (1792,
-    1792 and 1416 rows), and the gradient rows sit on every chunk edge. All of
+    must get dH = 0). The dZ budget splits the vocabulary into slices: bf16
+    three of up to 88320 rows (dZ read transposed for dH), fp32 twelve of up
+    to 23040 (row-major dZ); dH adds up the slices' products in place. The
+    gradient rows' targets sit on both sides of every slice boundary. All of
     dW and the gradient rows of dH against the oracle on those rows."""
     import linear_cross_entropy_amd as flce
     N, D, V = 5000, 64, 262144
+    vs = 88320 if dtype == "bf16" else 23040
     assert flce.flce_backward_workspace_bytes(N, D, V, dtype) > 0
     H, W, y = workloads.make_custom(N, D, V, dtype, seed=21, device=DEV)
-    rows = np.array([0, 7, 1791, 1792, 2559, 2560, 3583, 3584, 4991, 4999])
+    bounds = [b for k in range(1, -(-V // vs)) for b in (k * vs - 1, k * vs)]
+    rows = np.unique(np.concatenate([np.array([0, 7, 2559, 2560, 4991, 4999]),
+                                     np.linspace(8, 4990, len(bounds)).astype(np.int64)]))
+    tgt = np.array((bounds + [0, V - 1] * len(rows))[:len(rows)], dtype=np.int32)
+    y[torch.as_tensor(rows, device=DEV)] = torch.as_tensor(tgt, device=DEV)
     g = torch.zeros(N, dtype=torch.float32)
     g[torch.as_tensor(rows)] = torch.linspace(0.5, 1.25, len(rows))
     g = g.to(DEV)
