@@ -67,7 +67,8 @@ typedef enum {
   FLCE_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, small workspace */
   FLCE_ERR_UNSUPPORTED = -2, /* unknown dtype, D*elem not a multiple of 16, sizes past int32 */
   FLCE_ERR_HIP = -3,         /* a HIP runtime call or a kernel launch failed */
-  FLCE_ERR_OOM = -4          /* the stream-ordered workspace allocation failed */
+  FLCE_ERR_OOM = -4,         /* the stream-ordered workspace allocation failed */
+  FLCE_ERR_SCRATCH = -5      /* flce_forward_noalloc: the shape needs more than its static scratch */
 } flce_status_t;
 
 /* How a shape is split into work. Filled by flce_get_plan (diagnostics). */
@@ -108,6 +109,30 @@ int flce_forward_ws(const void* H, const void* W, const int32_t* targets,
                     int64_t N, int64_t D, int64_t V, int dtype,
                     float* loss_out, float* lse_out,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As flce_forward, for callers that cannot allocate device memory at all:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It calls no allocator (no hipMalloc, hipMallocAsync, hipFree or
+ * allocating library routine) and takes no workspace argument: its
+ * workspace is a static 16 MiB device array inside the library, one copy per
+ * GPU, held until the process ends (the current device's copy is located on
+ * its first call there; `stream` must belong to the current device).
+ *   - The shape must need at most 16 MiB of workspace, i.e.
+ *     flce_workspace_bytes(N, D, V, dtype) <= 16 << 20 (the production shape
+ *     N = 8192, D = 4096, V = 151936 needs 0.56 MB); a larger one returns
+ *     FLCE_ERR_SCRATCH and enqueues nothing.
+ *   - Every call on one GPU uses that GPU's one array, and nothing in it is
+ *     carried from call to call (each call writes every value it reads), so
+ *     calls on one GPU must not overlap: two calls in flight at once on
+ *     different streams of the same GPU race on the array. Serialize them
+ *     (one stream, or events).
+ *   - Results are bit-identical to flce_forward_ws for the same inputs (the
+ *     same kernels and plan). Other conventions as for flce_forward.
+ */
+int flce_forward_noalloc(const void* H, const void* W, const int32_t* targets,
+                         int64_t N, int64_t D, int64_t V, int dtype,
+                         float* loss_out, float* lse_out, void* stream);
 
 /*
  * The first of the two launches of flce_forward_ws, on its own: the fused

@@ -7,6 +7,7 @@ device memory and the stream. The functions keep the C names:
 
     flce_forward(H, W, targets, loss=None, lse=None, stream=None) -> (loss, lse)
     flce_forward_ws(H, W, targets, workspace, loss=None, lse=None, stream=None)
+    flce_forward_noalloc(H, W, targets, loss=None, lse=None, stream=None)
     flce_partials(H, W, targets, workspace, stream=None)
     flce_merge(targets, D, V, dtype, workspace, loss=None, lse=None, stream=None)
     flce_workspace_bytes(N, D, V, dtype) -> int
@@ -53,6 +54,7 @@ FLCE_ERR_INVALID_ARG = -1
 FLCE_ERR_UNSUPPORTED = -2
 FLCE_ERR_HIP = -3
 FLCE_ERR_OOM = -4
+FLCE_ERR_SCRATCH = -5
 
 _vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
 
@@ -60,6 +62,8 @@ _lib.flce_forward.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _
 _lib.flce_forward.restype = _i32
 _lib.flce_forward_ws.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]
 _lib.flce_forward_ws.restype = _i32
+_lib.flce_forward_noalloc.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]
+_lib.flce_forward_noalloc.restype = _i32
 _lib.flce_partials.argtypes = [_vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]
 _lib.flce_partials.restype = _i32
 _lib.flce_merge.argtypes = [_vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp, _sz, _vp]
@@ -99,7 +103,7 @@ class FlcePlan(ctypes.Structure):
 _lib.flce_get_plan.argtypes = [_i64, _i64, _i64, _i32, ctypes.POINTER(FlcePlan)]
 _lib.flce_get_plan.restype = _i32
 
-EXPORTED = ["flce_forward", "flce_forward_ws", "flce_partials", "flce_merge",
+EXPORTED = ["flce_forward", "flce_forward_ws", "flce_forward_noalloc", "flce_partials", "flce_merge",
             "flce_workspace_bytes", "flce_get_plan", "flce_status_string", "flce_version",
             "flce_backward", "flce_backward_workspace_bytes",
             "flce_forward_quant", "flce_forward_quant_workspace_bytes",
@@ -219,6 +223,21 @@ def flce_forward_ws(H, W, targets, ws, loss=None, lse=None, stream=None, want_ls
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_forward_ws")
     return loss, (lse if want_lse else None)
+
+
+def flce_forward_noalloc(H, W, targets, loss=None, lse=None, stream=None):
+    """flce_forward with the library's static scratch as workspace: the C call
+    allocates nothing (outputs not given are allocated here, by torch).
+    Shapes needing more than 16 MiB of workspace raise FlceError
+    (FLCE_ERR_SCRATCH); calls on one GPU must not overlap."""
+    N, D, V, dt = _check_inputs(H, W, targets)
+    loss = _out(loss, N, H.device, "loss")
+    lse = _out(lse, N, H.device, "lse")
+    rc = _lib.flce_forward_noalloc(_ptr(H), _ptr(W), _ptr(targets), N, D, V, dt, _ptr(loss), _ptr(lse),
+                                   _stream_ptr(stream, H.device))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward_noalloc")
+    return loss, lse
 
 
 def flce_partials(H, W, targets, ws, stream=None):

@@ -43,6 +43,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 #include <stdlib.h>
@@ -1534,6 +1535,40 @@ int launch_backward_quant(const QuantBwdPlan& qb, const void* H, const uint8_t* 
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+// ------------------------------------------------------------------ static scratch
+// flce_forward_noalloc's workspace: a file-scope device array, one copy per
+// GPU, held until the process ends. Host code never uses the array's name as
+// an address (on the host it is only a stand-in for the symbol): the device
+// address of each GPU's copy comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is what the kernels receive.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the device's first use).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FLCE_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return FLCE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FLCE_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLCE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -1547,6 +1582,7 @@ const char* flce_status_string(int status) {
     case FLCE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case FLCE_ERR_HIP: return "HIP runtime error";
     case FLCE_ERR_OOM: return "workspace allocation failed";
+    case FLCE_ERR_SCRATCH: return "shape needs more workspace than the static scratch holds (16 MiB)";
     default: return "unknown status";
   }
 }
@@ -1634,6 +1670,26 @@ int flce_forward(const void* H, const void* W, const int32_t* targets, int64_t N
   if (rc == FLCE_OK) rc = launch_merge(pl, targets, loss_out, lse_out, ws, s);
   if (hipFreeAsync(ws, s) != hipSuccess && rc == FLCE_OK) rc = FLCE_ERR_HIP;
   return rc;
+}
+
+int flce_forward_noalloc(const void* H, const void* W, const int32_t* targets, int64_t N, int64_t D, int64_t V,
+                         int dtype, float* loss_out, float* lse_out, void* stream) {
+  Plan pl;
+  int rc = make_plan(N, D, V, dtype, &pl);
+  if (rc != FLCE_OK) return rc;
+  if ((rc = check_inputs(H, W, targets, N)) != FLCE_OK) return rc;
+  if (N == 0) return FLCE_OK;
+  if (!loss_out || !aligned(loss_out, 4) || (lse_out && !aligned(lse_out, 4)))
+    return FLCE_ERR_INVALID_ARG;
+  if (pl.ws_bytes > kScratchBytes) return FLCE_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws)) != FLCE_OK) return rc;
+  // Every partial the merge reads (m and s per row and chunk, and the target
+  // logit of each row whose target is in [0, V)) is written by the partials
+  // launch of the same call, so nothing in the scratch needs clearing.
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = launch_partials(pl, H, W, targets, ws, s)) != FLCE_OK) return rc;
+  return launch_merge(pl, targets, loss_out, lse_out, ws, s);
 }
 
 size_t flce_backward_workspace_bytes(int64_t N, int64_t D, int64_t V, int dtype) {
