@@ -12,9 +12,16 @@ JSON line:
   cpu_baseline the float64 CPU oracle on a bounded row sample of the same
                workload, on the host's cores (a reported baseline only)
 
+After the W warm-up steps, untimed launches continue until the per-launch
+time has settled (two consecutive 10-launch medians within 0.5%, at most
+--settle-seconds), then exactly K steps are timed. The forward's line also
+carries mfma_ceiling: the sustained rate of the same matrix-core instruction
+with register operands, measured in the same run (libflce_ceiling.so).
+
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prod_bf16]
        python bench.py --backward ...   (the backward instead: one step = one
        flce_backward, 3 x 2*N*V*D FLOP, timed over all of its launches)
+       python bench.py --mfma-ceiling   (only the matrix-core ceiling)
 """
 from __future__ import annotations
 
@@ -69,7 +76,8 @@ def traffic_from_profile(workload: str):
     return {"fetch_bytes": t["fetch_bytes_per_launch"], "write_bytes": t["write_bytes_per_launch"],
             "total_bytes": t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"],
             "copy_scale": t.get("copy_scale"), "source": os.path.relpath(TRAFFIC_FILE, ROOT),
-            "what": "L2 fetches from the memory fabric (Infinity Cache hits + HBM) and writes, per launch"}
+            "what": "L2 fetches from and writes to the memory fabric per launch: an upper bound on HBM bytes "
+                    "(Infinity Cache hits are not separable on this part); the algorithmic bytes are the lower bound"}
 
 
 def cpu_baseline(H, W, y, w, target_seconds: float, max_rows: int):
@@ -149,6 +157,8 @@ def bench_backward(args, w):
     for _ in range(args.warmup):
         flce.flce_backward(H, W, y, lse, g, workspace=ws, dH=dH, dW=dW, stream=stream)
     torch.cuda.synchronize()
+    settled = settle(lambda: flce.flce_backward(H, W, y, lse, g, workspace=ws, dH=dH, dW=dW, stream=stream),
+                     stream, args.settle_seconds, block=4)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} backward steps", file=sys.stderr, flush=True)
@@ -197,6 +207,7 @@ def bench_backward(args, w):
             "kernel_ms_each": [round(t, 4) for t in each],
         },
         "outputs_finite": bool(torch.isfinite(dH).all().item() and torch.isfinite(dW).all().item()),
+        "settle": settled,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle's backward on a row sample", file=sys.stderr, flush=True)
@@ -216,6 +227,83 @@ def device_env():
     return {"hip": torch.version.hip, "torch": torch.__version__, "device": props.name,
             "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
             "hbm_bytes": props.total_memory, "host_threads": os.cpu_count()}
+
+
+def settle(launch, stream, seconds: float, block: int = 10, tol: float = 0.005):
+    """Untimed launches after the warm-up steps until the part's clock has
+    settled: blocks of `block` launches, each timed with HIP events on the
+    launch stream, until two consecutive block medians agree within `tol`, or
+    `seconds` have passed. (On a freshly leased part the first seconds of
+    launches can run a few percent slow and speed up as the power manager
+    settles.) Returns what was done, for the JSON line."""
+    import torch
+    t0 = time.perf_counter()
+    medians = []
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(block)]
+        for a, b in ev:
+            a.record(stream)
+            launch()
+            b.record(stream)
+        torch.cuda.synchronize()
+        n += block
+        ms = sorted(a.elapsed_time(b) for a, b in ev)
+        medians.append(ms[len(ms) // 2])
+        if len(medians) >= 2 and abs(medians[-1] - medians[-2]) <= tol * medians[-2]:
+            break
+    return {"launches": n, "seconds": round(time.perf_counter() - t0, 3),
+            "settled": len(medians) >= 2 and abs(medians[-1] - medians[-2]) <= tol * medians[-2],
+            "block_medians_ms": [round(m, 4) for m in medians]}
+
+
+def mfma_ceiling(seconds: float = 0.5, kind: str = "random"):
+    """The sustained rate of v_mfma_f32_32x32x16_bf16 with operands in
+    registers (libflce_ceiling.so), one workgroup of 8 waves per compute unit,
+    and the shader clock it held (s_memtime against the 100 MHz s_memrealtime).
+    Random operands toggle the datapath as real data does; constant ones show
+    the clock the part reaches when they do not."""
+    import torch
+    from linear_cross_entropy_amd import ceiling
+    dev = torch.device("cuda:0")
+    grid, threads = torch.cuda.get_device_properties(0).multi_processor_count, 512
+    n = grid * threads * 64
+    gen = torch.Generator(device=dev).manual_seed(123)
+    ops = (torch.randn(n, device=dev, generator=gen) if kind == "random"
+           else torch.ones(n, device=dev)).to(torch.bfloat16)
+    per_iter = grid * (threads // 64) * ceiling.MFMA_PER_ITER * ceiling.FLOP_PER_MFMA
+    iters = 2000
+    ceiling.flce_ceiling_mfma(ops, 0, iters, grid, threads)        # warm-up and rate probe
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    ceiling.flce_ceiling_mfma(ops, 0, iters, grid, threads)
+    b.record()
+    torch.cuda.synchronize()
+    iters = max(iters, int(iters * seconds * 1e3 / max(a.elapsed_time(b), 1e-3)))
+    a.record()
+    _, clk = ceiling.flce_ceiling_mfma(ops, 0, iters, grid, threads)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    c = clk.view(grid, 4).cpu().double()
+    ghz = float(((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2]) * 0.1).median())
+    tflops = per_iter * iters / (ms * 1e-3) / 1e12
+    return {"operands": kind, "tflops": tflops, "frac_of_peak": tflops / PEAK_TFLOPS["bf16"],
+            "shader_clock_ghz": ghz, "ms": ms, "mfma_per_launch": iters * grid * 8 * ceiling.MFMA_PER_ITER,
+            "kernel": "flce_ceiling_kernel<0> (libflce_ceiling.so)"}
+
+
+def bench_ceiling(args):
+    """--mfma-ceiling: the matrix-core ceiling with random and with constant
+    operands, one JSON line."""
+    rnd = mfma_ceiling(args.ceiling_seconds, "random")
+    const = mfma_ceiling(args.ceiling_seconds, "const")
+    print(json.dumps({
+        "metric": "sustained bf16 MFMA rate, register operands (v_mfma_f32_32x32x16_bf16)",
+        "value": rnd["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "higher_is_better": True,
+        "dtype": "bf16", "data": "synthetic (random N(0,1) bf16 operand fragments; and all-ones)",
+        "peak": PEAK_TFLOPS["bf16"], "random": rnd, "constant": const, "env": device_env()}), flush=True)
 
 
 def bench_quant(args, w):
@@ -263,6 +351,7 @@ def bench_quant(args, w):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settled = settle(step, stream, args.settle_seconds, block=4)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for a, b in ev:
@@ -308,6 +397,7 @@ def bench_quant(args, w):
         },
         "outputs_finite": bool(torch.isfinite(dH if args.backward else loss).all().item()),
         "cpu_baseline": None,
+        "settle": settled,
     }
     result["env"] = device_env()
     print(json.dumps(result))
@@ -331,6 +421,14 @@ def main():
                     help="time flce_forward_quant (with --backward: flce_backward_quant) with a BITS-bit head "
                          "of the workload's shape instead")
     ap.add_argument("--group", type=int, default=64, help="weights per scale/bias group with --quant")
+    ap.add_argument("--settle-seconds", type=float, default=4.0,
+                    help="after the warm-up steps, untimed launches until consecutive 10-launch medians agree "
+                         "within 0.5%% (at most this long)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="leave out the matrix-core ceiling measured beside the forward")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the matrix-core ceiling (random and constant operands)")
+    ap.add_argument("--ceiling-seconds", type=float, default=1.0)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -345,6 +443,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration, 5)
+        return
+    if args.mfma_ceiling:
+        bench_ceiling(args)
         return
 
     import linear_cross_entropy_amd as flce
@@ -374,6 +475,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    settled = settle(step, stream, args.settle_seconds)
+    print(f"[bench] settled after {settled['launches']} more launches ({settled['seconds']} s)",
+          file=sys.stderr, flush=True)
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -436,7 +540,13 @@ def main():
         },
         "outputs_finite": sanity,
         "kernel_source_sha": kernel_source_sha(),
+        "settle": settled,
     }
+    if not args.no_ceiling:
+        print("[bench] measuring the matrix-core ceiling", file=sys.stderr, flush=True)
+        ceil = mfma_ceiling(0.4, "random")
+        result["mfma_ceiling"] = {k: ceil[k] for k in ("tflops", "frac_of_peak", "shader_clock_ghz", "kernel")}
+        result["mfma_ceiling"]["kernel_frac_of_ceiling"] = achieved / ceil["tflops"]
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a row sample", file=sys.stderr, flush=True)
         cb = cpu_baseline(H, W, y, w, args.cpu_seconds, args.cpu_max_rows)

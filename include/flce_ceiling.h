@@ -23,8 +23,11 @@ extern "C" {
  * ops[(global thread index) * 8 + 0..7] -- ops must hold grid * threads * 8
  * such fragments, 16-byte aligned -- then runs `iters` iterations of 32
  * MFMAs over 8 accumulators:
- *   order 0: consecutive instructions write different accumulators;
- *   order 1: each accumulator takes 4 instructions back to back.
+ *   order 0: consecutive instructions write different accumulators and
+ *            differ in both operands;
+ *   order 1: each accumulator takes 4 instructions back to back;
+ *   order 2: as 0, with the A operand held for 8 consecutive instructions;
+ *   order 3: as 0, with both operands held for 8 consecutive instructions.
  * FLOP per launch = grid * (threads / 64) * iters * 32 * 32768.
  * out (float32, grid * threads) receives each thread's accumulator sum, so
  * the work cannot be removed. clocks (uint64, grid * 4) receives, per

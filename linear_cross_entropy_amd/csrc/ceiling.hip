@@ -19,7 +19,10 @@
 //   order 0: k outer, j inner -- consecutive MFMAs write different
 //            accumulators (as in the forward's tile loop);
 //   order 1: j outer, k inner -- each accumulator takes its 4 MFMAs back to
-//            back (a dependent chain on one accumulator).
+//            back (a dependent chain on one accumulator);
+//   orders 2 and 3: as order 0, with the A operand (2) or both operands (3)
+//            held for the 8 instructions of a k step, to measure what
+//            operand toggling between instructions costs.
 // Lane 0 of each workgroup records s_memtime (shader clock) and
 // s_memrealtime (the fixed 100 MHz reference) before and after its loop, so
 // the host can state the clock the part held.
