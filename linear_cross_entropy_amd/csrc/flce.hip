@@ -50,8 +50,11 @@
 #include <string.h>
 
 #include "flce.h"
+#include "flce_plan.h"
 
 namespace {
+
+using namespace flce_plan;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -73,48 +76,6 @@ constexpr int kRsrcWord3 = 0x00020000;
 // Any offset at or above num_records reads as zero; every resource built here
 // covers less than 2^31 bytes.
 constexpr uint32_t kOutOfRange = 0x80000000u;
-
-// ------------------------------------------------------------------ tiles
-// A tile configuration: BV vocabulary rows x BT tokens per workgroup, split
-// over WAVES_V x WAVES_T waves; each wave owns a (BV/WAVES_V) x (BT/WAVES_T)
-// block of 32x32 MFMA tiles. K is staged 128 bytes (64 bf16 / 32 fp32) at a
-// time, double-buffered in LDS; every wave fills BV/NW W rows and BT/NW H
-// rows of each stage.
-constexpr int kStageRowBytes = 128;
-
-template <int BV_, int BT_, int WAVES_V_, int WAVES_T_>
-struct TileCfg {
-  static constexpr int BV = BV_, BT = BT_, WAVES_V = WAVES_V_, WAVES_T = WAVES_T_;
-  static constexpr int NW = WAVES_V * WAVES_T;
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int WV = BV / WAVES_V;          // vocabulary rows per wave
-  static constexpr int WT = BT / WAVES_T;          // tokens per wave
-  static constexpr int MB = WV / 32;               // 32x32 MFMA tiles along vocabulary
-  static constexpr int NB = WT / 32;               // ... and along tokens
-  static constexpr int WROWS = BV / NW;            // W rows each wave fills per stage
-  static constexpr int HROWS = BT / NW;            // H rows each wave fills per stage
-  static constexpr int WLOADS = WROWS / 8;         // 16-byte loads per lane (8 rows each)
-  static constexpr int HLOADS = HROWS / 8;
-  static constexpr int STAGE_BYTES = (BV + BT) * kStageRowBytes;
-  static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  // Whether the younger wave of each SIMD takes issue priority around the
-  // stage barrier (see the main loop). Measured on the production shape: the
-  // 256-row tile is 3% faster with it, the 320- and 384-row tiles up to 1%
-  // faster without it.
-  static constexpr bool YOUNG_PRIO = BV == 256;
-  static_assert(WV % 32 == 0 && WT % 32 == 0, "waves own whole MFMA tiles");
-  static_assert(WROWS % 8 == 0 && HROWS % 8 == 0 && BV % 16 == 0, "whole 8-row loads");
-  static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
-};
-// All three run 8 waves (two per SIMD). Staged bytes per FLOP fall with the
-// tile, (BV + BT) / (BV * BT): 256x256 stages 512 rows per 65536 logits,
-// 320x256 576 per 81920 (-10%), 384x256 640 per 98304 (-17%). The staging
-// path (global -> LDS) is what bounds the kernel at large shapes, so the
-// largest tile that fills the machine wins; 384x256 takes the whole 160 KB
-// of LDS and 192 accumulator registers per lane.
-typedef TileCfg<256, 256, 2, 4> Tile256;
-typedef TileCfg<320, 256, 2, 4> Tile320;
-typedef TileCfg<384, 256, 2, 4> Tile384;
 
 // What the tile loop does with each finished tile of Z = A B^T (A: the rows
 // along the tile's vocabulary axis, B: the rows along its token axis).
@@ -956,140 +917,6 @@ __global__ __launch_bounds__(256) void flce_dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------ host side
-constexpr int kSlots = 256;       // workgroups resident at once: one per CU
-constexpr size_t kAlign = 256;
-
-enum TileId { kTile256 = 0, kTile320 = 1, kTile384 = 2 };
-
-struct Plan {
-  int N, V, row_bytes, dtype, tile;
-  int BV, BT, threads, lds_bytes;
-  int row_blocks, vocab_tiles, chunks, grid, xcd_rows, xcd_chunks;
-  size_t off_m, off_s, off_z, ws_bytes;
-};
-
-size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
-
-struct TileInfo {
-  int BV, BT, threads, lds_bytes;
-  int cost_per_logit;  // relative time per logit at large shapes (x1000), measured on MI355X
-};
-template <typename C>
-constexpr TileInfo tile_info(int cost) {
-  return TileInfo{C::BV, C::BT, C::THREADS, C::LDS_BYTES, cost};
-}
-// Per-logit costs from the production shape (N=8192, D=4096, V=151936):
-// 7.29, 7.13 and 7.05 ms for the same work with 256-, 320- and 384-row tiles.
-// (Across nine shapes from N=1024 to 16384, D=1024 to 8192, V=32000 to
-// 262144, the planner's pick was the fastest tile or within 4% of it.)
-constexpr TileInfo kTiles[3] = {tile_info<Tile256>(1034), tile_info<Tile320>(1011), tile_info<Tile384>(1000)};
-
-// Chunks per row block for a tile: minimise the makespan in tile-times,
-// ceil(row_blocks*c / slots) * ceil(vocab_tiles / c); ties go to fewer chunks.
-// Returns 0 when no chunk count keeps a chunk's W rows under 2^31 bytes.
-int best_chunks(int64_t row_blocks, int64_t vocab_tiles, int64_t BV, int64_t row_bytes, int64_t* makespan) {
-  int best_c = 0;
-  int64_t best_cost = INT64_MAX;
-  const int64_t RB = row_blocks > 0 ? row_blocks : 1;
-  for (int64_t c = 1; c <= vocab_tiles; ++c) {
-    const int64_t rounds = (RB * c + kSlots - 1) / kSlots;
-    const int64_t per = (vocab_tiles + c - 1) / c;
-    if (per * BV * row_bytes >= (int64_t(1) << 31)) continue;  // one buffer resource per chunk
-    const int64_t cost = rounds * per;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best_c = (int)c;
-    }
-  }
-  *makespan = best_cost;
-  return best_c;
-}
-
-// Tile configuration for a shape: fp32 always uses 256x256; for bf16 the
-// tile whose makespan (tile-times x logits per tile x cost per logit) is
-// smallest. FLCE_TILE=256, 320 or 384 in the environment forces a bf16
-// configuration (for tests and tuning; every configuration computes the same
-// result). No tile above max_tile is chosen (forced ones included).
-int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype, int max_tile) {
-  if (dtype != FLCE_BF16) return kTile256;
-  static const int forced = [] {
-    const char* e = getenv("FLCE_TILE");
-    const int v = e ? atoi(e) : 0;
-    return v == 256 ? kTile256 : v == 320 ? kTile320 : v == 384 ? kTile384 : -1;
-  }();
-  if (forced >= 0) return std::min(forced, max_tile);
-  int best = kTile256;
-  double best_t = 0;
-  for (int t = kTile256; t <= max_tile; ++t) {
-    const TileInfo& ti = kTiles[t];
-    int64_t makespan = 0;
-    if (best_chunks((N + ti.BT - 1) / ti.BT, (V + ti.BV - 1) / ti.BV, ti.BV, row_bytes, &makespan) == 0) continue;
-    const double est = (double)makespan * ti.BV * ti.BT * ti.cost_per_logit;
-    if (t == kTile256 || est < best_t) {
-      best = t;
-      best_t = est;
-    }
-  }
-  return best;
-}
-
-int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl, int max_tile = kTile384) {
-  if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
-  if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
-  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
-  const int64_t rb = D * es;
-  if (rb % 16 != 0) return FLCE_ERR_UNSUPPORTED;
-  pl->tile = choose_tile(N, V, rb, dtype, max_tile);
-  const TileInfo& ti = kTiles[pl->tile];
-  const int kBV = ti.BV, kBT = ti.BT;
-  pl->BV = kBV;
-  pl->BT = kBT;
-  pl->threads = ti.threads;
-  pl->lds_bytes = ti.lds_bytes;
-  // 32-bit offsets inside one tile's buffer resource, int32 indices elsewhere
-  if ((int64_t)kBV * rb >= (int64_t(1) << 31) || N > INT32_MAX / 2 || V > INT32_MAX - kBV)
-    return FLCE_ERR_UNSUPPORTED;
-  pl->N = (int)N;
-  pl->V = (int)V;
-  pl->row_bytes = (int)rb;
-  pl->dtype = dtype;
-  pl->row_blocks = (int)((N + kBT - 1) / kBT);
-  pl->vocab_tiles = (int)((V + kBV - 1) / kBV);
-  int64_t makespan = 0;
-  const int best_c = best_chunks(pl->row_blocks, pl->vocab_tiles, kBV, rb, &makespan);
-  if (best_c == 0) return FLCE_ERR_UNSUPPORTED;
-  const int RB = pl->row_blocks > 0 ? pl->row_blocks : 1;
-  pl->chunks = best_c;
-  pl->grid = RB * best_c;
-  // XCD groups: 8 equal blocks of the (row block, chunk) grid, each
-  // xcd_rows x xcd_chunks, chosen to minimise the distinct bytes of H and W
-  // one XCD touches per tile-time (proportional to xcd_rows*BT + xcd_chunks*BV).
-  pl->xcd_rows = 0;
-  pl->xcd_chunks = 0;
-  if (pl->grid % 8 == 0) {
-    int64_t best = INT64_MAX;
-    for (int gr = 1; gr <= RB; ++gr) {
-      if (RB % gr) continue;
-      const int per = pl->grid / 8;
-      if (per % gr) continue;
-      const int gc = per / gr;
-      if (best_c % gc) continue;
-      if ((RB / gr) * (best_c / gc) != 8) continue;
-      const int64_t cost = (int64_t)gr * kBT + (int64_t)gc * kBV;
-      if (cost < best) {
-        best = cost;
-        pl->xcd_rows = gr;
-        pl->xcd_chunks = gc;
-      }
-    }
-  }
-  pl->off_m = 0;
-  pl->off_s = align_up((size_t)best_c * N * sizeof(float));
-  pl->off_z = pl->off_s + align_up((size_t)best_c * N * sizeof(float));
-  pl->ws_bytes = pl->off_z + align_up((size_t)N * sizeof(float));
-  return FLCE_OK;
-}
-
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_inputs(const void* H, const void* W, const int32_t* y, int64_t N) {
@@ -1192,106 +1019,6 @@ int launch_merge(const Plan& pl, const int32_t* y, float* loss, float* lse, cons
 // N D, never with N V. Padding rows and columns (to 64 elements, so that rows
 // of the transposed copies start on 128-byte lines) are written as zeros, so
 // the products need no masks on K.
-constexpr double kDzBudget = 1024.0 * 1024 * 1024;
-
-// The launches of one vocabulary slice of Vs rows.
-struct SlicePlans {
-  int64_t Vs, Vsp;
-  Plan dz, dh, dw;     // dZ pass; dH product; dW product (dw unused when dW is not wanted)
-  int ksplit, ks_per;  // bf16 dH: K slices and k-stages per slice
-};
-
-struct BwdPlan {
-  int64_t N, D, V, Np, Vs;  // Vs: rows of every slice but the last
-  int dtype, slices;
-  size_t es;
-  SlicePlans full, last;
-  size_t off_wt, off_ht, off_dzt, off_dz, off_part, ws_bytes;
-};
-
-// K slices for the transposed-B dH product: when its tiles leave CUs idle,
-// split the contraction over V so that up to kSlots workgroups run, keeping
-// at least 16 k-stages (1024 of K) per slice and at most 16 slices.
-void gemmt_split(const Plan& ph, int* ksplit, int* ks_per) {
-  const int64_t grid = (int64_t)ph.row_blocks * ph.chunks;
-  const int ks_all = (ph.row_bytes + kStageRowBytes - 1) / kStageRowBytes;
-  int S = 1;
-  while (S < 16 && grid * (S + 1) <= kSlots && ks_all / (S + 1) >= 16) ++S;
-  const int per = (ks_all + S - 1) / S;
-  *ks_per = per;
-  *ksplit = (ks_all + per - 1) / per;
-}
-
-int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-
-// Plans of one slice's launches (N > 0). with_dw: plan the dW product too.
-int make_slice_plans(int64_t N, int64_t D, int64_t Vs, int64_t Np, int dtype, bool with_dw, SlicePlans* sp) {
-  sp->Vs = Vs;
-  sp->Vsp = round_up(Vs, 64);
-  sp->ksplit = 1;
-  sp->ks_per = 0;
-  int rc;
-  if ((rc = make_plan(N, D, Vs, dtype, &sp->dz)) != FLCE_OK) return rc;                     // dZ
-  if (dtype == FLCE_BF16) {
-    if ((rc = make_plan(N, sp->Vsp, D, dtype, &sp->dh, kTile320)) != FLCE_OK) return rc;    // dH (transposed B)
-    gemmt_split(sp->dh, &sp->ksplit, &sp->ks_per);
-  } else {
-    if ((rc = make_plan(D, sp->Vsp, N, dtype, &sp->dh)) != FLCE_OK) return rc;              // dH
-  }
-  if (with_dw && (rc = make_plan(D, Np, Vs, dtype, &sp->dw)) != FLCE_OK) return rc;        // dW
-  return FLCE_OK;
-}
-
-// Vocabulary rows per slice: every slice's dZ (dz_copies copies of Vsp x Np
-// elements) fits kDzBudget bytes, the slices are balanced, and a slice is a
-// multiple of 3840 rows (whole 256-, 320- and 384-row tiles) when that
-// leaves at least one such block, else of 64.
-int64_t slice_rows(int64_t V, int64_t Np, int64_t es, int dz_copies) {
-  const int64_t cap = (int64_t)(kDzBudget / ((double)Np * (double)es * dz_copies));
-  const int64_t gran = cap >= 3840 ? 3840 : 64;
-  const int64_t maxv = std::max<int64_t>(cap / gran * gran, 64);
-  if (V <= maxv) return V;
-  const int64_t n = (V + maxv - 1) / maxv;
-  return std::min(maxv, round_up((V + n - 1) / n, gran));
-}
-
-int make_bwd_plan(int64_t N, int64_t D, int64_t V, int dtype, BwdPlan* bp) {
-  if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
-  if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
-  const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
-  if ((D * es) % 16 != 0) return FLCE_ERR_UNSUPPORTED;
-  if (N > INT32_MAX / 2 || V > INT32_MAX / 2 || D > INT32_MAX / 2) return FLCE_ERR_UNSUPPORTED;
-  bp->N = N;
-  bp->D = D;
-  bp->V = V;
-  bp->dtype = dtype;
-  bp->es = (size_t)es;
-  bp->Np = round_up(N, 64);
-  // a stage of the transposed B (64 k-rows of dzt) stays under 2^31 bytes
-  if (bp->Np * es * 64 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
-  bp->Vs = slice_rows(V, bp->Np, es, dtype == FLCE_BF16 ? 1 : 2);
-  bp->slices = N > 0 ? (int)((V + bp->Vs - 1) / bp->Vs) : 0;
-  int rc;
-  if (N > 0) {
-    if ((rc = make_slice_plans(N, D, bp->Vs, bp->Np, dtype, true, &bp->full)) != FLCE_OK) return rc;
-    if ((rc = make_slice_plans(N, D, V - (int64_t)(bp->slices - 1) * bp->Vs, bp->Np, dtype, true, &bp->last)) !=
-        FLCE_OK)
-      return rc;
-  } else {
-    bp->full.Vsp = bp->last.Vsp = 0;
-    bp->full.ksplit = bp->last.ksplit = 1;
-  }
-  const int64_t vsp = bp->full.Vsp;
-  if (vsp * es >= (int64_t(1) << 31) || bp->Np * es >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
-  const int parts = std::max(bp->full.ksplit, bp->last.ksplit);
-  bp->off_wt = 0;
-  bp->off_ht = align_up((size_t)(D * vsp * es));
-  bp->off_dzt = bp->off_ht + align_up((size_t)(D * bp->Np * es));
-  bp->off_dz = bp->off_dzt + align_up((size_t)(vsp * bp->Np * es));
-  bp->off_part = bp->off_dz + (dtype == FLCE_BF16 ? 0 : align_up((size_t)(bp->Np * vsp * es)));
-  bp->ws_bytes = bp->off_part + (parts > 1 ? align_up((size_t)parts * (size_t)(N * D) * 4) : 0);
-  return FLCE_OK;
-}
 
 template <typename T>
 void launch_transpose(const void* in, int rows, int cols, int64_t ld_in, void* out, int64_t ld_out,
@@ -1400,43 +1127,6 @@ int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32
 // offset by the slice's first row), then one merge covers every chunk. Vs is
 // a multiple of 3072 rows (8 chunks of 384-row tiles) with the buffer near
 // kQuantSliceBytes; a vocabulary that fits one slice is a single pass.
-constexpr double kQuantSliceBytes = 256.0 * 1024 * 1024;
-
-struct QuantPlan {
-  int64_t N, D, V, Vs;
-  int bits, group, slices, chunks_total;
-  Plan full, last;  // plans of a full slice and of the last one
-  size_t off_buf, off_m, off_s, off_z, ws_bytes;
-};
-
-int make_quant_plan(int64_t N, int64_t D, int64_t V, int bits, int group, QuantPlan* qp) {
-  if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
-  if ((bits != 4 && bits != 8) || group < 8 || group % 8 != 0 || D % group != 0) return FLCE_ERR_UNSUPPORTED;
-  qp->N = N;
-  qp->D = D;
-  qp->V = V;
-  qp->bits = bits;
-  qp->group = group;
-  int64_t vs = (int64_t)(kQuantSliceBytes / (double)(D * 2)) / 3072 * 3072;
-  if (vs < 3072) vs = 3072;
-  qp->Vs = std::min(vs, V);
-  qp->slices = (int)((V + qp->Vs - 1) / qp->Vs);
-  int rc;
-  if ((rc = make_plan(N, D, qp->Vs, FLCE_BF16, &qp->full)) != FLCE_OK) return rc;
-  const int64_t v_last = V - (int64_t)(qp->slices - 1) * qp->Vs;
-  if ((rc = make_plan(N, D, v_last, FLCE_BF16, &qp->last)) != FLCE_OK) return rc;
-  if (V > INT32_MAX / 2) return FLCE_ERR_UNSUPPORTED;
-  const int64_t C = (int64_t)(qp->slices - 1) * qp->full.chunks + qp->last.chunks;
-  if (C > INT32_MAX) return FLCE_ERR_UNSUPPORTED;
-  qp->chunks_total = (int)C;
-  qp->off_buf = 0;
-  qp->off_m = align_up((size_t)(qp->Vs * D * 2));
-  qp->off_s = qp->off_m + align_up((size_t)C * N * sizeof(float));
-  qp->off_z = qp->off_s + align_up((size_t)C * N * sizeof(float));
-  qp->ws_bytes = qp->off_z + align_up((size_t)N * sizeof(float));
-  return FLCE_OK;
-}
-
 void launch_dequant(int bits, int D, int group, const uint8_t* codes, const float* scales, const float* biases,
                     int64_t rows, __bf16* out, hipStream_t stream) {
   const int64_t n = rows * (D / 8);
@@ -1483,40 +1173,6 @@ int launch_forward_quant(const QuantPlan& qp, const void* H, const uint8_t* code
 // vocabulary runs in slices as in the dense backward (backward_slice without
 // dW), each first dequantised into the workspace; a slice is at most the
 // forward's dequantisation slice and keeps dZ^T within kDzBudget.
-struct QuantBwdPlan {
-  int64_t N, D, V, Np, Vs;
-  int bits, group, slices;
-  SlicePlans full, last;
-  size_t off_w, off_wt, off_dzt, off_part, ws_bytes;
-};
-
-int make_quant_bwd_plan(int64_t N, int64_t D, int64_t V, int bits, int group, QuantBwdPlan* qb) {
-  int rc;
-  QuantPlan q;
-  if ((rc = make_quant_plan(N, D, V, bits, group, &q)) != FLCE_OK) return rc;
-  qb->N = N;
-  qb->D = D;
-  qb->V = V;
-  qb->bits = bits;
-  qb->group = group;
-  qb->Np = round_up(N, 64);
-  if (qb->Np * 2 * 64 >= (int64_t(1) << 31)) return FLCE_ERR_UNSUPPORTED;
-  qb->Vs = std::min(q.Vs, slice_rows(V, qb->Np, 2, 1));
-  qb->slices = (int)((V + qb->Vs - 1) / qb->Vs);
-  if ((rc = make_slice_plans(N, D, qb->Vs, qb->Np, FLCE_BF16, false, &qb->full)) != FLCE_OK) return rc;
-  if ((rc = make_slice_plans(N, D, V - (int64_t)(qb->slices - 1) * qb->Vs, qb->Np, FLCE_BF16, false, &qb->last)) !=
-      FLCE_OK)
-    return rc;
-  const int64_t vsp = qb->full.Vsp;
-  const int parts = std::max(qb->full.ksplit, qb->last.ksplit);
-  qb->off_w = 0;
-  qb->off_wt = align_up((size_t)(qb->Vs * D * 2));
-  qb->off_dzt = qb->off_wt + align_up((size_t)(D * vsp * 2));
-  qb->off_part = qb->off_dzt + align_up((size_t)(vsp * qb->Np * 2));
-  qb->ws_bytes = qb->off_part + (parts > 1 ? align_up((size_t)parts * (size_t)(N * D) * 4) : 0);
-  return FLCE_OK;
-}
-
 int launch_backward_quant(const QuantBwdPlan& qb, const void* H, const uint8_t* codes, const float* scales,
                           const float* biases, const int32_t* y, const float* lse, const float* grad, float* dH,
                           void* ws, hipStream_t stream) {
