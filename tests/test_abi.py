@@ -171,11 +171,11 @@ def _up(x, m):
 
 def _slice_rows(N, V, es, copies):
     """Vocabulary rows per slice: the largest balanced size whose dZ buffers
-    (copies x Vsp x Np elements) fit the budget, in multiples of 3840 rows (or
+    (copies x Vsp x Np elements) fit the budget, in multiples of 6144 rows (or
     64 when the budget holds fewer)."""
     Np = _up(N, 64)
     cap = DZ_BUDGET // (Np * es * copies)
-    gran = 3840 if cap >= 3840 else 64
+    gran = 6144 if cap >= 6144 else 64
     maxv = max(cap // gran * gran, 64)
     if V <= maxv:
         return V
@@ -208,10 +208,10 @@ def test_backward_workspace_layout(flce):
     assert splits[(4, 8, 10, 0)] == 1                # too little K to split
     assert flce.flce_backward_workspace_bytes(4, 12, 10, 0) == 0   # unsupported D
     # the slicing itself: the production shape takes three slices, the stress shape five;
-    # the GPU test of ragged rows and slices relies on 88320 (bf16) and 23040 (fp32)
-    assert _slice_rows(8192, 151936, 2, 1) == 53760
+    # the GPU test of ragged rows and slices relies on 92160 (bf16) and 24576 (fp32)
+    assert _slice_rows(8192, 151936, 2, 1) == 55296
     assert -(-262144 // _slice_rows(8192, 262144, 2, 1)) == 5
-    assert _slice_rows(5000, 262144, 2, 1) == 88320 and _slice_rows(5000, 262144, 4, 2) == 23040
+    assert _slice_rows(5000, 262144, 2, 1) == 92160 and _slice_rows(5000, 262144, 4, 2) == 24576
 
 
 @pytest.mark.parametrize("N,D,V", [(8192, 4096, 151936), (8192, 8192, 262144), (65536, 4096, 151936),
