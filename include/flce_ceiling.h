@@ -27,8 +27,11 @@ extern "C" {
  *            differ in both operands;
  *   order 1: each accumulator takes 4 instructions back to back;
  *   order 2: as 0, with the A operand held for 8 consecutive instructions;
- *   order 3: as 0, with both operands held for 8 consecutive instructions.
- * FLOP per launch = grid * (threads / 64) * iters * 32 * 32768.
+ *   order 3: as 0, with both operands held for 8 consecutive instructions;
+ *   order 4: the same FLOP as 64 v_mfma_f32_16x16x32_bf16 per iteration (16x16
+ *            outputs, K = 32) over 32 accumulators of 4 registers, operands
+ *            varied as in order 0.
+ * FLOP per launch = grid * (threads / 64) * iters * 32 * 32768 (every order).
  * out (float32, grid * threads) receives each thread's accumulator sum, so
  * the work cannot be removed. clocks (uint64, grid * 4) receives, per
  * workgroup, s_memtime before and after the loop, then s_memrealtime (a

@@ -22,7 +22,9 @@
 //            back (a dependent chain on one accumulator);
 //   orders 2 and 3: as order 0, with the A operand (2) or both operands (3)
 //            held for the 8 instructions of a k step, to measure what
-//            operand toggling between instructions costs.
+//            operand toggling between instructions costs;
+//   order 4: the same FLOP on v_mfma_f32_16x16x32_bf16 (16x16 outputs, K =
+//            32, half the FLOP of one 32x32x16), twice as many instructions.
 // Lane 0 of each workgroup records s_memtime (shader clock) and
 // s_memrealtime (the fixed 100 MHz reference) before and after its loop, so
 // the host can state the clock the part held.
@@ -35,6 +37,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int ORDER>
@@ -81,12 +84,27 @@ __global__ __launch_bounds__(512, 1) void flce_ceiling_kernel(const bf16x8* __re
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[(k + 2 * j + (j >> 2)) & 3], acc[j], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-    } else {
+    } else if constexpr (ORDER == 3) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[k], b[k], acc[j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // order 4: the same FLOP as 64 v_mfma_f32_16x16x32_bf16 (16x16 outputs,
+      // K = 32) over 32 accumulators of 4 registers (the same 128 registers)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          f32x4 c = {acc[j >> 1][4 * (j & 1) + 0], acc[j >> 1][4 * (j & 1) + 1], acc[j >> 1][4 * (j & 1) + 2],
+                     acc[j >> 1][4 * (j & 1) + 3]};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(j + k) & 3], b[(k + 2 * j) & 3], c, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j >> 1][4 * (j & 1) + r] = c[r];
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -113,12 +131,13 @@ extern "C" {
 
 int flce_ceiling_mfma(const void* ops, int order, int64_t iters, int grid, int threads, int lds_bytes, float* out,
                       unsigned long long* clocks, void* stream) {
-  if (!ops || !out || !clocks || grid < 1 || iters < 1 || order < 0 || order > 3) return -1;
+  if (!ops || !out || !clocks || grid < 1 || iters < 1 || order < 0 || order > 4) return -1;
   if (threads < 64 || threads > 512 || threads % 64 != 0 || lds_bytes < 0 || lds_bytes > 160 * 1024) return -1;
   if ((uintptr_t)ops % 16 != 0) return -1;
   hipStream_t s = (hipStream_t)stream;
-  const void* fn[4] = {(const void*)flce_ceiling_kernel<0>, (const void*)flce_ceiling_kernel<1>,
-                       (const void*)flce_ceiling_kernel<2>, (const void*)flce_ceiling_kernel<3>};
+  const void* fn[5] = {(const void*)flce_ceiling_kernel<0>, (const void*)flce_ceiling_kernel<1>,
+                       (const void*)flce_ceiling_kernel<2>, (const void*)flce_ceiling_kernel<3>,
+                       (const void*)flce_ceiling_kernel<4>};
   if (lds_bytes > 64 * 1024 &&
       hipFuncSetAttribute(fn[order], hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess)
     return -3;
@@ -127,7 +146,8 @@ int flce_ceiling_mfma(const void* ops, int order, int64_t iters, int grid, int t
     case 0: hipLaunchKernelGGL((flce_ceiling_kernel<0>), dim3(grid), dim3(threads), lds_bytes, s, o, iters, out, clocks); break;
     case 1: hipLaunchKernelGGL((flce_ceiling_kernel<1>), dim3(grid), dim3(threads), lds_bytes, s, o, iters, out, clocks); break;
     case 2: hipLaunchKernelGGL((flce_ceiling_kernel<2>), dim3(grid), dim3(threads), lds_bytes, s, o, iters, out, clocks); break;
-    default: hipLaunchKernelGGL((flce_ceiling_kernel<3>), dim3(grid), dim3(threads), lds_bytes, s, o, iters, out, clocks); break;
+    case 3: hipLaunchKernelGGL((flce_ceiling_kernel<3>), dim3(grid), dim3(threads), lds_bytes, s, o, iters, out, clocks); break;
+    default: hipLaunchKernelGGL((flce_ceiling_kernel<4>), dim3(grid), dim3(threads), lds_bytes, s, o, iters, out, clocks); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
