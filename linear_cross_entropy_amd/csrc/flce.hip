@@ -63,7 +63,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_inff();
-constexpr f32x16 kZero16 = {};
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
@@ -121,21 +120,32 @@ struct TileArgs {
   int accumulate;
 };
 
-// Element-type specific pieces: a 16-byte fragment and the matrix-core step
-// that consumes one fragment of A and one of B (32x32 output, K = 16 bf16 or
-// 4 x K = 2 fp32).
-template <typename T> struct Mma;
+// Element-type and MFMA-shape specific pieces: a 16-byte fragment, the
+// accumulator of one M x M output tile, and the matrix-core step that
+// consumes one fragment of A and one of B (bf16: 32x32 outputs with K = 16,
+// or 16x16 outputs with K = 32; fp32: 32x32 outputs as 4 x K = 2).
+template <typename T, int M> struct Mma;
 
-template <> struct Mma<__bf16> {
+template <> struct Mma<__bf16, 32> {
   typedef bf16x8 frag;
-  static __device__ __forceinline__ f32x16 step(frag a, frag b, f32x16 c) {
+  typedef f32x16 acc;
+  static __device__ __forceinline__ acc step(frag a, frag b, acc c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
 };
 
-template <> struct Mma<float> {
+template <> struct Mma<__bf16, 16> {
+  typedef bf16x8 frag;
+  typedef f32x4 acc;
+  static __device__ __forceinline__ acc step(frag a, frag b, acc c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float, 32> {
   typedef f32x4 frag;
-  static __device__ __forceinline__ f32x16 step(frag a, frag b, f32x16 c) {
+  typedef f32x16 acc;
+  static __device__ __forceinline__ acc step(frag a, frag b, acc c) {
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
@@ -200,9 +210,19 @@ __device__ __forceinline__ void store4(char* dst, const float (&q)[4]) {
 // and hands the finished tile, in registers, to the MODE's epilogue.
 template <typename T, typename C, int MODE>
 __device__ __forceinline__ void tile_loop(const TileArgs& p) {
-  typedef typename Mma<T>::frag Frag;
+  typedef Mma<T, C::M> MmaT;
+  typedef typename MmaT::frag Frag;
+  typedef typename MmaT::acc Acc;
   constexpr int kBV = C::BV, kBT = C::BT, kWavesV = C::WAVES_V;
   constexpr int WV = C::WV, WT = C::WT, MB = C::MB, NB = C::NB;
+  // MFMA shape: M x M output tiles, KSTEPS instructions' K per 128-byte stage,
+  // ACC accumulator registers per lane and tile, KCH 16-byte chunks of a row
+  // per K step. Output layout of an M x M tile: lane l holds column l % M;
+  // register r holds row lane_row + row_in(r), lane_row = 4 (l / M) for both
+  // shapes (32x32: row_in(r) = 8 (r / 4) + r % 4; 16x16: row_in(r) = r).
+  constexpr int M = C::M, KSTEPS = C::KSTEPS, ACC = C::ACC, KCH = 64 / M;
+  static_assert(M == 32 || sizeof(T) == 2, "fp32 runs the 32x32 shape");
+  constexpr Acc kZeroAcc = {};
   constexpr int WLOADS = C::WLOADS, HLOADS = C::HLOADS;
   constexpr int kStageBytes = C::STAGE_BYTES;
 
@@ -291,6 +311,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   constexpr int kBRowBytes = kBT * 2;
   if constexpr (MODE == kGemmT) {
     static_assert(sizeof(T) == 2 && 64 * kBRowBytes == kBT * kStageRowBytes, "transposed B: bf16, 64 k-rows a stage");
+    static_assert(M == 32, "transposed B: 32x32 fragments");
 #pragma unroll
     for (int i = 0; i < HLOADS; ++i) {
       const int krow = 2 * (wave * HLOADS + i) + (lane >> 5);
@@ -364,18 +385,20 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     }
   };
 
-  // ---- fragment addresses: a 32x32xK MFMA tile reads, per lane, row
-  // (lane % 32) of its 32-row block and 16-byte chunk 2*kb + lane/32.
-  int koff[4];
+  // ---- fragment addresses: an M x M MFMA tile's operand fragment for K step
+  // kb is, per lane, row (lane % M) of its M-row block and 16-byte chunk
+  // KCH*kb + lane/M of the stage row (32x32: 2 kb + lane/32; 16x16: 4 kb + lane/16).
+  int koff[KSTEPS];
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-    koff[kb] = (lane & 31) * kStageRowBytes + (((2 * kb + (lane >> 5)) ^ swizzle(lane & 31)) * 16);
+  for (int kb = 0; kb < KSTEPS; ++kb)
+    koff[kb] = (lane % M) * kStageRowBytes + (((KCH * kb + lane / M) ^ swizzle(lane % M)) * 16);
   const int a_row = wv * WV;
   const int b_row = kBV + wt * WT;
 
-  // ---- per-lane online state for the NB token columns this lane holds.
-  // 32x32 MFMA output layout: lane l holds column l%32 and, in register r,
-  // row 8*(r/4) + 4*(l/32) + r%4 of the 32x32 tile.
+  // ---- per-lane online state for the NB token columns this lane holds
+  // (column l % M of each M x M tile; see the output layout above).
+  const int lane_row = 4 * (lane / M);
+  auto row_in = [](int r) { return M == 32 ? 8 * (r >> 2) + (r & 3) : r; };
   float m_run[NB], s_run[NB];
   int ytok[NB];
   float l2tok[NB], gtok[NB];  // kDz: lse * log2(e) and the upstream gradient of each token
@@ -383,7 +406,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   for (int nb = 0; nb < NB; ++nb) {
     m_run[nb] = kNegInf;
     s_run[nb] = 0.f;
-    const int tok = t0 + wt * WT + nb * 32 + (lane & 31);
+    const int tok = t0 + wt * WT + nb * M + (lane % M);
     ytok[nb] = -1;
     l2tok[nb] = 0.f;
     gtok[nb] = 0.f;
@@ -398,14 +421,14 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     }
   }
 
-  f32x16 acc[MB][NB];
+  Acc acc[MB][NB];
   // Fragments: the NB H fragments of the current k-block and of the next one
   // (two sets), and a rolling window of kASlots W fragments. W fragment q of
   // a stage (q = kb*MB + mb) lives in slot q % kASlots; once the MFMAs that
   // use it have issued, the slot receives fragment q + kASlots, and across
   // the stage boundary fragment j of the next stage (QN is a multiple of
   // kASlots, so that is slot j again).
-  constexpr int QN = 4 * MB;  // W fragments per stage
+  constexpr int QN = KSTEPS * MB;  // W fragments per stage
   constexpr int kASlots = QN % 3 == 0 ? 3 : 4;
   static_assert(QN % kASlots == 0 && MB >= kASlots, "rolling window");
   // kGemmT keeps all four k-blocks' B fragments of a stage (see the main loop)
@@ -413,7 +436,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   constexpr int kBSets = kTB ? 4 : 2;
   Frag fa[kASlots], fb[kBSets][NB];
   auto read_a = [&](const char* sb, int q) {
-    fa[q % kASlots] = *(const Frag*)(sb + (a_row + (q % MB) * 32) * kStageRowBytes + koff[q / MB]);
+    fa[q % kASlots] = *(const Frag*)(sb + (a_row + (q % MB) * M) * kStageRowBytes + koff[q / MB]);
   };
   // kGemmT: a B fragment (column n = lane % 32, k = 8 (lane / 32) + 0..7) is
   // two transposing reads of 4 k each. Within a 16-lane group, lane s names
@@ -448,7 +471,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     } else {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        fb[kb % kBSets][nb] = *(const Frag*)(sb + (b_row + nb * 32) * kStageRowBytes + koff[kb]);
+        fb[kb % kBSets][nb] = *(const Frag*)(sb + (b_row + nb * M) * kStageRowBytes + koff[kb]);
     }
   };
   constexpr int STEPS = NB * (sizeof(T) == 2 ? 1 : 4);  // matrix instructions per W fragment
@@ -514,7 +537,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
           const int kb = q / MB, mb = q % MB;
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = Mma<T>::step(fa[q % kASlots], fb[kb % kBSets][nb], (kFirst && kb == 0) ? kZero16 : acc[mb][nb]);
+            acc[mb][nb] = MmaT::step(fa[q % kASlots], fb[kb % kBSets][nb], (kFirst && kb == 0) ? kZeroAcc : acc[mb][nb]);
           if constexpr (kTB) {
             if (q == 0) {
               read_b(sb, 1);
@@ -522,7 +545,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
               read_b(sb, 3);
             }
           } else {
-            if (mb == 0 && kb + 1 < 4) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
+            if (mb == 0 && kb + 1 < KSTEPS) read_b(sb, kb + 1);  // the other set was last used by k-block kb - 1
           }
           read_a(sb, q + kASlots);
           if constexpr (kTB) {
@@ -539,7 +562,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 6 * NB, 0);      // k-blocks 1-3 of B (two reads each)
             __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
-          } else if (!kTB && mb == 0 && kb + 1 < 4) {
+          } else if (!kTB && mb == 0 && kb + 1 < KSTEPS) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);           // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, NB, 0);          // next k-block's H fragments
             __builtin_amdgcn_sched_group_barrier(0x008, STEPS - 1, 0);
@@ -575,7 +598,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       for (int j = 0; j < kASlots; ++j) {
         const int q = QN - kASlots + j;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = Mma<T>::step(fa[j], fb[3 % kBSets][nb], acc[q % MB][nb]);
+        for (int nb = 0; nb < NB; ++nb) acc[q % MB][nb] = MmaT::step(fa[j], fb[(KSTEPS - 1) % kBSets][nb], acc[q % MB][nb]);
         if (j == 0) read_b(sn, 0);
         read_a(sn, j);
         if constexpr (!kTB) issue_one(tbuf, j, more2);
@@ -598,46 +621,46 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       // ---- epilogue of one vocabulary tile, entirely in registers
       if (vw + WV > p.V) {
         // ragged last tile: vocabulary rows >= V are not logits at all
-        int lim = p.V - vw - 4 * (lane >> 5);
+        int lim = p.V - vw - lane_row;
         asm volatile("" : "+v"(lim));  // compared here, not hoisted as per-register lane masks
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (mb * 32 + 8 * (r >> 2) + (r & 3) >= lim) acc[mb][nb][r] = kNegInf;
+            for (int r = 0; r < ACC; ++r)
+              if (mb * M + row_in(r) >= lim) acc[mb][nb][r] = kNegInf;
       }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // target logit: written by the one lane holding (y, token), in this (rare, divergent) branch
         const int rel = ytok[nb] - vw;
-        if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & 1) == (lane >> 5)) {
+        if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & (64 / M - 1)) == lane / M) {
           int want = rel;
           asm volatile("" : "+v"(want));  // likewise
-          const int want_mb = want >> 5;
-          const int want_r = ((want & 31) >> 3) * 4 + (want & 3);
+          const int want_mb = want / M;
+          const int want_r = M == 32 ? ((want & 31) >> 3) * 4 + (want & 3) : (want & 3);
           float val = 0.f;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
+            for (int r = 0; r < ACC; ++r)
               if (mb == want_mb && r == want_r) val = acc[mb][nb][r];
-          p.z_target[t0 + wt * WT + nb * 32 + (lane & 31)] = val;
+          p.z_target[t0 + wt * WT + nb * M + (lane % M)] = val;
         }
         // online update: m' = max(m, m_tile), s' = s e^(m - m') + sum_j e^(z_j - m')
         float tmax = kNegInf;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
+          for (int r = 0; r < ACC; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
         const float m_new = fmaxf(m_run[nb], tmax);
         const float c = (m_new == kNegInf) ? 0.f : off2(m_new);
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
+          for (int r = 0; r < ACC; r += 2) {
             s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], kLog2e, -c));
             s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r + 1], kLog2e, -c));
           }
@@ -648,18 +671,18 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       // ---- dZ = g (softmax(Z) - onehot(y)) of one tile, with
       // softmax = 2^(z log2(e) - lse log2(e)); rows >= V and tokens >= N are 0.
       // Written to dz[tok][v] (four consecutive v per lane and register group)
-      // and dzt[v][tok] (32 consecutive tokens per half-wave).
-      const int v_lane = vw + 4 * (lane >> 5);
+      // and dzt[v][tok] (M consecutive tokens per M lanes).
+      const int v_lane = vw + lane_row;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int tok = t0 + wt * WT + nb * 32 + (lane & 31);
+        const int tok = t0 + wt * WT + nb * M + (lane % M);
         if (tok >= p.dz_rows) continue;
         const bool tok_ok = tok < p.N;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int v0 = v_lane + mb * 32 + 8 * r4;   // rows v0 .. v0 + 3 in registers 4*r4 ..
+          for (int r4 = 0; r4 < ACC / 4; ++r4) {
+            const int v0 = v_lane + mb * M + 8 * r4;   // rows v0 .. v0 + 3 in registers 4*r4 ..
             if (v0 >= p.dz_cols) continue;
             T q[4];
 #pragma unroll
@@ -687,7 +710,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int a0 = vw + mb * 32 + 8 * r4 + 4 * (lane >> 5);
+            const int a0 = vw + mb * 32 + 8 * r4 + lane_row;
             if (a0 >= p.V) continue;
             float q[4] = {acc[mb][nb][4 * r4], acc[mb][nb][4 * r4 + 1], acc[mb][nb][4 * r4 + 2],
                           acc[mb][nb][4 * r4 + 3]};
@@ -704,13 +727,13 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
       // ---- C[a][b] = Z (or C[a][b] + Z) for a < V, b < N
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int b = t0 + wt * WT + nb * 32 + (lane & 31);
+        const int b = t0 + wt * WT + nb * M + (lane % M);
         if (b >= p.N) continue;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int a = vw + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          for (int r = 0; r < ACC; ++r) {
+            const int a = vw + mb * M + row_in(r) + lane_row;
             if (a < p.V) {
               float* dst = p.C + (size_t)a * p.ldc + b;
               *dst = p.accumulate ? *dst + acc[mb][nb][r] : acc[mb][nb][r];
@@ -725,30 +748,32 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 
   if constexpr (MODE != kForward) return;
 
-  // ---- end of chunk: combine the two half-waves, then the kWavesV waves that
-  // share a token range, in a fixed order (deterministic), and write one
-  // (m, s) per token.
+  // ---- end of chunk: combine the 64 / M lanes that hold the same token
+  // column (xor M, then xor 2M), then the kWavesV waves that share a token
+  // range, in a fixed order (deterministic), and write one (m, s) per token.
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const float m2 = __shfl_xor(m_run[nb], 32);
-    const float s2 = __shfl_xor(s_run[nb], 32);
-    combine(m_run[nb], s_run[nb], m2, s2);
-  }
-  __syncthreads();  // every wave is done with the stage buffers
-  float* red = (float*)smem;  // [kWavesV][kBT] m, then [kWavesV][kBT] s
-  if (lane < 32) {
+  for (int x = M; x < 64; x *= 2)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wt * WT + nb * 32 + lane;
+      const float m2 = __shfl_xor(m_run[nb], x);
+      const float s2 = __shfl_xor(s_run[nb], x);
+      combine(m_run[nb], s_run[nb], m2, s2);
+    }
+  __syncthreads();  // every wave is done with the stage buffers
+  float* red = (float*)smem;  // [kWavesV][kBT] m, then [kWavesV][kBT] s
+  if (lane < M) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wt * WT + nb * M + lane;
       red[wv * kBT + col] = m_run[nb];
       red[(kWavesV + wv) * kBT + col] = s_run[nb];
     }
   }
   __syncthreads();
-  if (wv == 0 && lane < 32) {
+  if (wv == 0 && lane < M) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wt * WT + nb * 32 + lane;
+      const int col = wt * WT + nb * M + lane;
       float m = red[col], s = red[kWavesV * kBT + col];
 #pragma unroll
       for (int w = 1; w < kWavesV; ++w) combine(m, s, red[w * kBT + col], red[(kWavesV + w) * kBT + col]);
@@ -957,9 +982,9 @@ TileArgs tile_args(const Plan& pl, const void* B, const void* A) {
     else if ((pl).tile == kTile384)                                                                     \
       hipLaunchKernelGGL((KERNEL<__bf16, Tile384>), dim3((pl).grid), dim3(Tile384::THREADS), 0, stream, args); \
     else if ((pl).tile == kTile320)                                                                     \
-      hipLaunchKernelGGL((KERNEL<__bf16, Tile320>), dim3((pl).grid), dim3(Tile320::THREADS), 0, stream, args); \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile320h>), dim3((pl).grid), dim3(Tile320h::THREADS), 0, stream, args); \
     else                                                                                                \
-      hipLaunchKernelGGL((KERNEL<__bf16, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args); \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile256h>), dim3((pl).grid), dim3(Tile256h::THREADS), 0, stream, args); \
   } while (0)
 
 // The transposed-B product: bf16 only, and at most the 320-row tile (its four

@@ -19,20 +19,23 @@ namespace flce_plan {
 // ------------------------------------------------------------------ tiles
 // A tile configuration: BV vocabulary rows x BT tokens per workgroup, split
 // over WAVES_V x WAVES_T waves; each wave owns a (BV/WAVES_V) x (BT/WAVES_T)
-// block of 32x32 MFMA tiles. K is staged 128 bytes (64 bf16 / 32 fp32) at a
-// time, double-buffered in LDS; every wave fills BV/NW W rows and BT/NW H
-// rows of each stage.
+// block of M x M MFMA tiles (M = 32: v_mfma_f32_32x32x16_bf16, K = 16 per
+// instruction; M = 16: v_mfma_f32_16x16x32_bf16, K = 32). K is staged 128
+// bytes (64 bf16 / 32 fp32) at a time, double-buffered in LDS; every wave
+// fills BV/NW W rows and BT/NW H rows of each stage.
 constexpr int kStageRowBytes = 128;
 
-template <int BV_, int BT_, int WAVES_V_, int WAVES_T_>
+template <int BV_, int BT_, int WAVES_V_, int WAVES_T_, int M_ = 32>
 struct TileCfg {
-  static constexpr int BV = BV_, BT = BT_, WAVES_V = WAVES_V_, WAVES_T = WAVES_T_;
+  static constexpr int BV = BV_, BT = BT_, WAVES_V = WAVES_V_, WAVES_T = WAVES_T_, M = M_;
   static constexpr int NW = WAVES_V * WAVES_T;
   static constexpr int THREADS = 64 * NW;
   static constexpr int WV = BV / WAVES_V;          // vocabulary rows per wave
   static constexpr int WT = BT / WAVES_T;          // tokens per wave
-  static constexpr int MB = WV / 32;               // 32x32 MFMA tiles along vocabulary
-  static constexpr int NB = WT / 32;               // ... and along tokens
+  static constexpr int MB = WV / M;                // M x M MFMA tiles along vocabulary
+  static constexpr int NB = WT / M;                // ... and along tokens
+  static constexpr int KSTEPS = M / 8;             // MFMA K steps per 128-byte stage (bf16): 4 or 2
+  static constexpr int ACC = M * M / 64;           // accumulator registers per lane and MFMA tile
   static constexpr int WROWS = BV / NW;            // W rows each wave fills per stage
   static constexpr int HROWS = BT / NW;            // H rows each wave fills per stage
   static constexpr int WLOADS = WROWS / 8;         // 16-byte loads per lane (8 rows each)
@@ -44,19 +47,33 @@ struct TileCfg {
   // 256-row tile is 3% faster with it, the 320- and 384-row tiles up to 1%
   // faster without it.
   static constexpr bool YOUNG_PRIO = BV == 256;
-  static_assert(WV % 32 == 0 && WT % 32 == 0, "waves own whole MFMA tiles");
+  static_assert(M == 32 || M == 16, "MFMA shape");
+  static_assert(WV % M == 0 && WT % M == 0, "waves own whole MFMA tiles");
   static_assert(WROWS % 8 == 0 && HROWS % 8 == 0 && BV % 16 == 0, "whole 8-row loads");
   static_assert(LDS_BYTES <= 160 * 1024, "gfx950 LDS");
 };
-// All three run 8 waves (two per SIMD). Staged bytes per FLOP fall with the
-// tile, (BV + BT) / (BV * BT): 256x256 stages 512 rows per 65536 logits,
-// 320x256 576 per 81920 (-10%), 384x256 640 per 98304 (-17%). The staging
-// path (global -> LDS) is what bounds the kernel at large shapes, so the
-// largest tile that fills the machine wins; 384x256 takes the whole 160 KB
-// of LDS and 192 accumulator registers per lane.
-typedef TileCfg<256, 256, 2, 4> Tile256;
-typedef TileCfg<320, 256, 2, 4> Tile320;
-typedef TileCfg<384, 256, 2, 4> Tile384;
+// All run 8 waves (two per SIMD). Staged bytes per FLOP fall with the tile,
+// (BV + BT) / (BV * BT): 256x256 stages 512 rows per 65536 logits, 320x256
+// 576 per 81920 (-10%), 384x256 640 per 98304 (-17%); 384x256 takes the whole
+// 160 KB of LDS and 192 accumulator registers per lane.
+//
+// The MFMA shape matters as much. The part holds its power limit by lowering
+// the clock, and with random operands the 16x16x32 bf16 instruction runs at a
+// ~15% higher clock than the 32x32x16 one for the same FLOP (less register
+// traffic per FLOP: a quarter of the accumulator bytes per instruction for
+// half the FLOP). Measured on the production shape, one box, alternating
+// launches: 384x256 with 32x32 tiles 6.93 ms; 320x256 with 16x16 tiles 6.70
+// ms; 256x256 with 16x16 7.02 ms, with 32x32 7.29 ms. The 16x16 shape holds
+// four token columns per lane instead of two (more B fragments and more
+// per-token state), so at 384x256 it no longer fits the register file
+// without spilling in the stage loop: the bf16 tiles are 256x256 and
+// 320x256 with 16x16 MFMAs and 384x256 with 32x32 ones. fp32 and the
+// transposed-B product run 32x32 tiles.
+typedef TileCfg<256, 256, 2, 4> Tile256;        // 32x32: fp32, and the transposed-B dH product
+typedef TileCfg<320, 256, 2, 4> Tile320;        // 32x32: the transposed-B dH product
+typedef TileCfg<384, 256, 2, 4> Tile384;        // 32x32
+typedef TileCfg<256, 256, 2, 4, 16> Tile256h;   // 16x16
+typedef TileCfg<320, 256, 2, 4, 16> Tile320h;   // 16x16
 
 
 // ------------------------------------------------------------------ forward plan
@@ -82,11 +99,12 @@ template <typename C>
 constexpr TileInfo tile_info(int cost) {
   return TileInfo{C::BV, C::BT, C::THREADS, C::LDS_BYTES, cost};
 }
-// Per-logit costs from the production shape (N=8192, D=4096, V=151936):
-// 7.29, 7.13 and 7.05 ms for the same work with 256-, 320- and 384-row tiles.
-// (Across nine shapes from N=1024 to 16384, D=1024 to 8192, V=32000 to
-// 262144, the planner's pick was the fastest tile or within 4% of it.)
-constexpr TileInfo kTiles[3] = {tile_info<Tile256>(1034), tile_info<Tile320>(1011), tile_info<Tile384>(1000)};
+// Per-logit costs of the bf16 tiles from the production shape (N=8192,
+// D=4096, V=151936), one box, alternating launches: 7.02 ms (256x256, 16x16
+// MFMAs), 6.70 ms (320x256, 16x16) and 6.93 ms (384x256, 32x32) for the same
+// work. The geometry (BV, BT, threads, LDS) of a tile id is the same for
+// fp32, which runs 32x32 MFMAs on the 256x256 tile.
+constexpr TileInfo kTiles[3] = {tile_info<Tile256h>(1048), tile_info<Tile320h>(1000), tile_info<Tile384>(1035)};
 
 // Chunks per row block for a tile: minimise the makespan in tile-times,
 // ceil(row_blocks*c / slots) * ceil(vocab_tiles / c); ties go to fewer chunks.

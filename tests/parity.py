@@ -69,16 +69,17 @@ EDGE = [
     (64, 1024, 32001, "bf16"),
     (64, 1024, 31999, "bf16"),
     (40, 256, 50257, "bf16"),
-    (1000, 136, 100003, "bf16"),   # 320x256 tile: ragged rows, vocabulary and K
-    (4096, 64, 65536, "bf16"),     # 384x256 tile, one k-stage per tile, ragged vocabulary
-    (3000, 64, 120000, "bf16"),    # 384x256 tile without the XCD remap, ragged rows and vocabulary
+    (1000, 136, 100003, "bf16"),   # 320x256 tile (16x16 MFMAs): ragged rows, vocabulary and K
+    (4096, 64, 65536, "bf16"),     # 320x256 tile with the XCD remap, one k-stage per tile, ragged vocabulary
+    (3000, 64, 120000, "bf16"),    # 320x256 tile without the XCD remap, ragged rows
+    (3000, 64, 30000, "bf16"),     # 384x256 tile (32x32 MFMAs) with the XCD remap, ragged rows and vocabulary
     (1, 4, 1, "fp32"),
     (5, 36, 300, "fp32"),
     (257, 128, 1025, "fp32"),
 ]
 
 # (N, D, V) for the tile- and chunk-boundary target test, one per tile size
-BOUNDARY_SHAPES = [(512, 256, 50257), (1024, 64, 151936), (4096, 64, 65536)]
+BOUNDARY_SHAPES = [(512, 256, 50257), (1024, 64, 151936), (3000, 64, 30000)]
 
 
 

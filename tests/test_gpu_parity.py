@@ -135,7 +135,11 @@ def test_targets_on_tile_and_chunk_boundaries(N, D, V):
     for c in range(1, C):
         s = (c * base + min(c, rem)) * BV
         marks.update({s - 1, s})
-    for sub in (31, 32, 63, 64, 127, 128):
+    # every row position inside the first MFMA tiles (16x16: 4 lane groups x
+    # 4 registers; 32x32: 2 x 16), both 32-row blocks' edges, and the edge
+    # between the two waves that split a tile's vocabulary
+    marks.update(range(0, 48))
+    for sub in (63, 64, 127, 128, BV // 2 - 1, BV // 2, BV // 2 + 15, BV // 2 + 16):
         marks.add(sub)
     marks = sorted(m for m in marks if 0 <= m < V)
     H, W, _ = workloads.make_custom(N, D, V, "bf16", seed=11, device=DEV)
