@@ -987,6 +987,19 @@ TileArgs tile_args(const Plan& pl, const void* B, const void* A) {
       hipLaunchKernelGGL((KERNEL<__bf16, Tile256h>), dim3((pl).grid), dim3(Tile256h::THREADS), 0, stream, args); \
   } while (0)
 
+// The backward's launches: 32x32 tiles for every tile id.
+#define FLCE_LAUNCH_TILES_M32(KERNEL, pl, args, stream)                                                 \
+  do {                                                                                                  \
+    if ((pl).dtype == FLCE_FP32)                                                                        \
+      hipLaunchKernelGGL((KERNEL<float, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args);  \
+    else if ((pl).tile == kTile384)                                                                     \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile384>), dim3((pl).grid), dim3(Tile384::THREADS), 0, stream, args); \
+    else if ((pl).tile == kTile320)                                                                     \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile320>), dim3((pl).grid), dim3(Tile320::THREADS), 0, stream, args); \
+    else                                                                                                \
+      hipLaunchKernelGGL((KERNEL<__bf16, Tile256>), dim3((pl).grid), dim3(Tile256::THREADS), 0, stream, args); \
+  } while (0)
+
 // The transposed-B product: bf16 only, and at most the 320-row tile (its four
 // sets of B fragments do not fit the 384-row tile's registers).
 #define FLCE_LAUNCH_TILES_GEMMT(KERNEL, pl, args, stream)                                               \
@@ -1090,7 +1103,7 @@ void backward_slice(const SlicePlans& sp, int dtype, int64_t N, int64_t D, int64
   a.dzt_ld = (int)Np;
   a.dz_rows = (int)Np;
   a.dz_cols = (int)sp.Vsp;
-  FLCE_LAUNCH_TILES(flce_dz_kernel, sp.dz, a, stream);
+  FLCE_LAUNCH_TILES_M32(flce_dz_kernel, sp.dz, a, stream);
   if (bf) {
     // dH[token][d] (+)= sum_v dZ[token][v] W_s[v][d]: A = W_s^T, B = dZ read from dzt
     TileArgs g = tile_args(sp.dh, b.dzt, b.wt);
@@ -1110,14 +1123,14 @@ void backward_slice(const SlicePlans& sp, int dtype, int64_t N, int64_t D, int64
     g.C = dH;
     g.ldc = (int)D;
     g.accumulate = first ? 0 : 1;
-    FLCE_LAUNCH_TILES(flce_gemm_kernel, sp.dh, g, stream);
+    FLCE_LAUNCH_TILES_M32(flce_gemm_kernel, sp.dh, g, stream);
   }
   if (dWs) {
     // dW_s[v][d] = sum_token dzt[v][token] H^T[d][token]: A = dzt, B = H^T
     TileArgs w = tile_args(sp.dw, b.ht, b.dzt);
     w.C = dWs;
     w.ldc = (int)D;
-    FLCE_LAUNCH_TILES(flce_gemm_kernel, sp.dw, w, stream);
+    FLCE_LAUNCH_TILES_M32(flce_gemm_kernel, sp.dw, w, stream);
   }
 }
 

@@ -105,6 +105,13 @@ constexpr TileInfo tile_info(int cost) {
 // work. The geometry (BV, BT, threads, LDS) of a tile id is the same for
 // fp32, which runs 32x32 MFMAs on the 256x256 tile.
 constexpr TileInfo kTiles[3] = {tile_info<Tile256h>(1048), tile_info<Tile320h>(1000), tile_info<Tile384>(1035)};
+// The backward's launches (the dZ pass and the products) run 32x32 tiles at
+// every size: its time goes to storing dZ and to the dH product rather than
+// to the matrix cores' clock, and with 16x16 tiles it was no faster (25.95
+// and 26.00 ms against 25.72 ms at the production shape). Their per-logit
+// costs: 7.29, 7.13 and 7.05 ms for the same work with 256-, 320- and
+// 384-row 32x32 tiles.
+constexpr TileInfo kTilesM32[3] = {tile_info<Tile256>(1034), tile_info<Tile320>(1011), tile_info<Tile384>(1000)};
 
 // Chunks per row block for a tile: minimise the makespan in tile-times,
 // ceil(row_blocks*c / slots) * ceil(vocab_tiles / c); ties go to fewer chunks.
@@ -132,7 +139,7 @@ inline int best_chunks(int64_t row_blocks, int64_t vocab_tiles, int64_t BV, int6
 // smallest. FLCE_TILE=256, 320 or 384 in the environment forces a bf16
 // configuration (for tests and tuning; every configuration computes the same
 // result). No tile above max_tile is chosen (forced ones included).
-inline int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype, int max_tile) {
+inline int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype, int max_tile, const TileInfo* tiles) {
   if (dtype != FLCE_BF16) return kTile256;
   static const int forced = [] {
     const char* e = getenv("FLCE_TILE");
@@ -143,7 +150,7 @@ inline int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype, int m
   int best = kTile256;
   double best_t = 0;
   for (int t = kTile256; t <= max_tile; ++t) {
-    const TileInfo& ti = kTiles[t];
+    const TileInfo& ti = tiles[t];
     int64_t makespan = 0;
     if (best_chunks((N + ti.BT - 1) / ti.BT, (V + ti.BV - 1) / ti.BV, ti.BV, row_bytes, &makespan) == 0) continue;
     const double est = (double)makespan * ti.BV * ti.BT * ti.cost_per_logit;
@@ -155,7 +162,10 @@ inline int choose_tile(int64_t N, int64_t V, int64_t row_bytes, int dtype, int m
   return best;
 }
 
-inline int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl, int max_tile = kTile384) {
+// m32: plan for 32x32-MFMA tiles (the backward's launches); otherwise for the
+// forward's tiles (16x16 MFMAs at 256 and 320 rows).
+inline int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl, int max_tile = kTile384,
+                     bool m32 = false) {
   if (dtype != FLCE_BF16 && dtype != FLCE_FP32) return FLCE_ERR_UNSUPPORTED;
   if (N < 0 || D < 1 || V < 1) return FLCE_ERR_INVALID_ARG;
   // int32 indices and 32-bit buffer offsets: larger sizes are refused before
@@ -164,8 +174,9 @@ inline int make_plan(int64_t N, int64_t D, int64_t V, int dtype, Plan* pl, int m
   const int64_t es = dtype == FLCE_BF16 ? 2 : 4;
   const int64_t rb = D * es;
   if (rb % 16 != 0) return FLCE_ERR_UNSUPPORTED;
-  pl->tile = choose_tile(N, V, rb, dtype, max_tile);
-  const TileInfo& ti = kTiles[pl->tile];
+  const TileInfo* tiles = m32 ? kTilesM32 : kTiles;
+  pl->tile = choose_tile(N, V, rb, dtype, max_tile, tiles);
+  const TileInfo& ti = tiles[pl->tile];
   const int kBV = ti.BV, kBT = ti.BT;
   pl->BV = kBV;
   pl->BT = kBT;
@@ -257,14 +268,14 @@ inline int make_slice_plans(int64_t N, int64_t D, int64_t Vs, int64_t Np, int dt
   sp->ksplit = 1;
   sp->ks_per = 0;
   int rc;
-  if ((rc = make_plan(N, D, Vs, dtype, &sp->dz)) != FLCE_OK) return rc;                     // dZ
+  if ((rc = make_plan(N, D, Vs, dtype, &sp->dz, kTile384, true)) != FLCE_OK) return rc;                 // dZ
   if (dtype == FLCE_BF16) {
-    if ((rc = make_plan(N, sp->Vsp, D, dtype, &sp->dh, kTile320)) != FLCE_OK) return rc;    // dH (transposed B)
+    if ((rc = make_plan(N, sp->Vsp, D, dtype, &sp->dh, kTile320, true)) != FLCE_OK) return rc;          // dH (transposed B)
     gemmt_split(sp->dh, &sp->ksplit, &sp->ks_per);
   } else {
-    if ((rc = make_plan(D, sp->Vsp, N, dtype, &sp->dh)) != FLCE_OK) return rc;              // dH
+    if ((rc = make_plan(D, sp->Vsp, N, dtype, &sp->dh, kTile384, true)) != FLCE_OK) return rc;          // dH
   }
-  if (with_dw && (rc = make_plan(D, Np, Vs, dtype, &sp->dw)) != FLCE_OK) return rc;        // dW
+  if (with_dw && (rc = make_plan(D, Np, Vs, dtype, &sp->dw, kTile384, true)) != FLCE_OK) return rc;    // dW
   return FLCE_OK;
 }
 
