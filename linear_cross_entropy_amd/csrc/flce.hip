@@ -226,7 +226,18 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   constexpr int WLOADS = C::WLOADS, HLOADS = C::HLOADS;
   constexpr int kStageBytes = C::STAGE_BYTES;
 
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  // The forward on 16x16 tiles keeps the workgroup's targets in LDS beside the
+  // stages (kBT ints) instead of in registers: a lane holds four token
+  // columns there, and the registers are needed for the accumulators and
+  // fragments (held in registers, the targets were spilled and reloaded every
+  // tile, each reload waiting for the next stage's loads as well).
+  // The running maxima go there too (one float per lane and token column),
+  // when they fit: held across the stage loop but used only once per tile,
+  // they were the other values spilled.
+  constexpr bool kYLds = MODE == kForward && M == 16 && C::LDS_BYTES + kBT * 4 <= 160 * 1024;
+  constexpr int kMLdsBytes = C::NW * NB * 64 * 4;
+  constexpr bool kMLds = kYLds && C::LDS_BYTES + kBT * 4 + kMLdsBytes <= 160 * 1024;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES + (kYLds ? kBT * 4 : 0) + (kMLds ? kMLdsBytes : 0)];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -399,18 +410,20 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   // (column l % M of each M x M tile; see the output layout above).
   const int lane_row = 4 * (lane / M);
   auto row_in = [](int r) { return M == 32 ? 8 * (r >> 2) + (r & 3) : r; };
-  float m_run[NB], s_run[NB];
-  int ytok[NB];
+  float m_run[NB], s_run[NB];  // m_run unused with kMLds
+  int ytok[NB];  // unused with kYLds
+  float* msm = (float*)(smem + C::LDS_BYTES + kBT * 4) + wave * NB * 64 + lane;  // kMLds: running max of column nb at [nb * 64]
   float l2tok[NB], gtok[NB];  // kDz: lse * log2(e) and the upstream gradient of each token
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     m_run[nb] = kNegInf;
+    if constexpr (kMLds) msm[nb * 64] = kNegInf;  // read only after the prologue's barrier
     s_run[nb] = 0.f;
     const int tok = t0 + wt * WT + nb * M + (lane % M);
     ytok[nb] = -1;
     l2tok[nb] = 0.f;
     gtok[nb] = 0.f;
-    if constexpr (MODE == kForward || MODE == kDz) {
+    if constexpr ((MODE == kForward && !kYLds) || MODE == kDz) {
       if (tok < p.N) ytok[nb] = p.y[tok] - p.v_off;
     }
     if constexpr (MODE == kDz) {
@@ -502,6 +515,10 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
   if constexpr (!kTB) {
 #pragma unroll
     for (int i = 0; i < kASlots; ++i) issue_one(1, i, 1 < total);
+  }
+  int* ysm = (int*)(smem + C::LDS_BYTES);  // kYLds: target of token t0 + t (minus v_off), -1 past N
+  if constexpr (kYLds) {
+    for (int t = threadIdx.x; t < kBT; t += C::THREADS) ysm[t] = t0 + t < p.N ? p.y[t0 + t] - p.v_off : -1;
   }
   FLCE_WAIT_VMCNT(0);
   __syncthreads();
@@ -634,7 +651,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // target logit: written by the one lane holding (y, token), in this (rare, divergent) branch
-        const int rel = ytok[nb] - vw;
+        const int rel = (kYLds ? ysm[wt * WT + nb * M + (lane % M)] : ytok[nb]) - vw;
         if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & (64 / M - 1)) == lane / M) {
           int want = rel;
           asm volatile("" : "+v"(want));  // likewise
@@ -654,7 +671,8 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < ACC; ++r) tmax = fmaxf(tmax, acc[mb][nb][r]);
-        const float m_new = fmaxf(m_run[nb], tmax);
+        const float m_old = kMLds ? msm[nb * 64] : m_run[nb];
+        const float m_new = fmaxf(m_old, tmax);
         const float c = (m_new == kNegInf) ? 0.f : off2(m_new);
         float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -664,8 +682,11 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
             s0 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], kLog2e, -c));
             s1 += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r + 1], kLog2e, -c));
           }
-        s_run[nb] = s_run[nb] * __builtin_amdgcn_exp2f(off2(m_run[nb]) - c) + (s0 + s1);
-        m_run[nb] = m_new;
+        s_run[nb] = s_run[nb] * __builtin_amdgcn_exp2f(off2(m_old) - c) + (s0 + s1);
+        if constexpr (kMLds)
+          msm[nb * 64] = m_new;
+        else
+          m_run[nb] = m_new;
       }
     } else if constexpr (MODE == kDz) {
       // ---- dZ = g (softmax(Z) - onehot(y)) of one tile, with
@@ -748,6 +769,10 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 
   if constexpr (MODE != kForward) return;
 
+  if constexpr (kMLds) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) m_run[nb] = msm[nb * 64];
+  }
   // ---- end of chunk: combine the 64 / M lanes that hold the same token
   // column (xor M, then xor 2M), then the kWavesV waves that share a token
   // range, in a fixed order (deterministic), and write one (m, s) per token.
