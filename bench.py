@@ -16,7 +16,10 @@ After the W warm-up steps, untimed launches continue until the per-launch
 time has settled (two consecutive 10-launch medians within 0.5%, at most
 --settle-seconds), then exactly K steps are timed. The forward's line also
 carries mfma_ceiling: the sustained rate of the same matrix-core instruction
-with register operands, measured in the same run (libflce_ceiling.so).
+with register operands, measured in the same run (libflce_ceiling.so), and,
+for the production workload, also_measured: the backward, the 4-bit quantised
+head's forward and the small and medium workloads, each timed the same way
+with fewer steps (--no-extra leaves them out).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prod_bf16]
        python bench.py --backward ...   (the backward instead: one step = one
@@ -215,7 +218,7 @@ def bench_backward(args, w):
     else:
         result["cpu_baseline"] = None
     result["env"] = device_env()
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def device_env():
@@ -410,7 +413,7 @@ def bench_quant(args, w):
         "settle": settled,
     }
     result["env"] = device_env()
-    print(json.dumps(result))
+    return result
 
 
 def main():
@@ -439,6 +442,9 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the matrix-core ceiling (random and constant operands)")
     ap.add_argument("--ceiling-seconds", type=float, default=1.0)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the headline forward (no also_measured block)")
+    ap.add_argument("--also-steps", type=int, default=10, help="timed steps of each also_measured configuration")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -458,16 +464,69 @@ def main():
         bench_ceiling(args)
         return
 
-    import linear_cross_entropy_amd as flce
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
     if args.quant:
-        bench_quant(args, w)
+        print(json.dumps(bench_quant(args, w)), flush=True)
         return
     if args.backward:
-        bench_backward(args, w)
+        print(json.dumps(bench_backward(args, w)), flush=True)
         return
+    result = bench_forward(args, w)
+    if not args.no_extra and w.name == "prod_bf16":
+        result["also_measured"] = also_measured(args)
+    print(json.dumps(result), flush=True)
+
+
+# The other configurations timed in the default run, after the headline
+# forward (each with its own warm-up and settle phase, fewer steps, no CPU
+# baseline): (label, workload, backward?, quantised-head bits)
+ALSO = (
+    ("backward_prod_bf16", "prod_bf16", True, 0),
+    ("forward_quant4_prod_bf16", "prod_bf16", False, 4),
+    ("forward_small_bf16", "small_bf16", False, 0),
+    ("forward_medium_bf16", "medium_bf16", False, 0),
+    ("backward_small_bf16", "small_bf16", True, 0),
+    ("backward_medium_bf16", "medium_bf16", True, 0),
+)
+
+
+def also_measured(args):
+    """Compact lines for the configurations in ALSO: the same measurements as
+    --backward, --quant 4 and --workload give, with the HIP-event kernel time
+    and its fraction of the bf16 dense peak."""
+    import workloads
+    out = {}
+    for label, wname, backward, bits in ALSO:
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup, sub.settle_seconds = args.also_steps, 2, min(args.settle_seconds, 2.0)
+        sub.no_cpu_baseline, sub.no_ceiling, sub.backward, sub.quant = True, True, backward, bits
+        w = workloads.WORKLOADS[wname]
+        print(f"[bench] also: {label}", file=sys.stderr, flush=True)
+        if bits:
+            r = bench_quant(sub, w)
+        elif backward:
+            r = bench_backward(sub, w)
+        else:
+            r = bench_forward(sub, w)
+        rl = r["roofline"]
+        out[label] = {"metric": r["metric"], "kernel": rl["kernel"], "steps": sub.steps,
+                      "kernel_ms_avg": rl["kernel_ms_avg"], "kernel_ms_median": rl["kernel_ms_median"],
+                      "achieved_tflops": rl["achieved"], "frac": rl["frac"], "tokens_per_s": r["value"],
+                      "settled": r["settle"]["settled"], "outputs_finite": r["outputs_finite"]}
+        if "tile_vocab" in r["config"]:
+            out[label]["tile"] = f'{r["config"]["tile_vocab"]}x{r["config"]["tile_tokens"]}'
+            out[label]["chunks"] = r["config"]["chunks"]
+    return out
+
+
+def bench_forward(args, w):
+    """One step = flce_partials + flce_merge over the workload; the partials
+    launch is the timed kernel."""
+    import torch
+    import linear_cross_entropy_amd as flce
+    import workloads
     dev = torch.device("cuda:0")
     print(f"[bench] generating {w.describe()}", file=sys.stderr, flush=True)
     H, W, y = workloads.make(w, dev)
@@ -571,7 +630,7 @@ def main():
     else:
         result["cpu_baseline"] = None
     result["env"] = device_env()
-    print(json.dumps(result), flush=True)
+    return result
 
 
 if __name__ == "__main__":

@@ -186,7 +186,7 @@ int flce_merge(const int32_t* targets, int64_t N, int64_t D, int64_t V, int dtyp
  *     elements); for bf16 shapes whose dH product alone would leave compute
  *     units idle, also S x N x D float32 partial sums of dH (2 <= S <= 16
  *     pieces of a slice's contraction, added in order). No O(N x V) memory:
- *     1.39 GB in all at N = 8192, D = 4096, V = 151936 in bf16, where the
+ *     1.43 GB in all at N = 8192, D = 4096, V = 151936 in bf16, where the
  *     fp32 logits alone would take 4.98 GB. Allocates nothing.
  *   - Other conventions (alignment, D * sizeof(element) % 16 == 0, stream,
  *     status codes) as for the forward.
