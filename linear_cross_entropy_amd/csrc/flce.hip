@@ -635,10 +635,16 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
     const int vw = (tile_begin + tile) * kBV + a_row;   // first A row (vocabulary row) of this wave
     ++tile;
     if constexpr (MODE == kForward) {
-      // ---- epilogue of one vocabulary tile, entirely in registers
+      // ---- epilogue of one vocabulary tile, entirely in registers. The
+      // lane's index is taken afresh here (mbcnt on an opaque all-ones mask,
+      // so that nothing derived from it is hoisted and kept live across the
+      // stage loop, where it had been spilled).
+      unsigned all = ~0u;
+      asm volatile("" : "+s"(all));
+      const int ln = (int)__builtin_amdgcn_mbcnt_hi(all, __builtin_amdgcn_mbcnt_lo(all, 0u));
       if (vw + WV > p.V) {
         // ragged last tile: vocabulary rows >= V are not logits at all
-        int lim = p.V - vw - lane_row;
+        int lim = p.V - vw - 4 * (ln / M);
         asm volatile("" : "+v"(lim));  // compared here, not hoisted as per-register lane masks
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -651,8 +657,8 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         // target logit: written by the one lane holding (y, token), in this (rare, divergent) branch
-        const int rel = (kYLds ? ysm[wt * WT + nb * M + (lane % M)] : ytok[nb]) - vw;
-        if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & (64 / M - 1)) == lane / M) {
+        const int rel = (kYLds ? ysm[wt * WT + nb * M + (ln % M)] : ytok[nb]) - vw;
+        if ((unsigned)rel < (unsigned)WV && ((rel >> 2) & (64 / M - 1)) == ln / M) {
           int want = rel;
           asm volatile("" : "+v"(want));  // likewise
           const int want_mb = want / M;
@@ -663,7 +669,7 @@ __device__ __forceinline__ void tile_loop(const TileArgs& p) {
 #pragma unroll
             for (int r = 0; r < ACC; ++r)
               if (mb == want_mb && r == want_r) val = acc[mb][nb][r];
-          p.z_target[t0 + wt * WT + nb * M + (lane % M)] = val;
+          p.z_target[t0 + wt * WT + nb * M + (ln % M)] = val;
         }
         // online update: m' = max(m, m_tile), s' = s e^(m - m') + sum_j e^(z_j - m')
         float tmax = kNegInf;
