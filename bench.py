@@ -18,7 +18,8 @@ time has settled (two consecutive 10-launch medians within 0.5%, at most
 carries mfma_ceiling: the sustained rate of the same matrix-core instruction
 with register operands, measured in the same run (libflce_ceiling.so), and,
 for the production workload, also_measured: the backward, the 4-bit quantised
-head's forward and the small and medium workloads, each timed the same way
+head's forward, the small and medium workloads, and cold-cache forwards
+(--cold: a 512 MiB read before each timed launch), each timed the same way
 with fewer steps (--no-extra leaves them out).
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload prod_bf16]
@@ -42,6 +43,7 @@ sys.path.insert(0, ROOT)
 # 4096 FLOP/clk/CU), fp32 matrix 157.3.
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}
 HBM_PEAK_GBS = 8000.0
+COLD_SCRUB_BYTES = 512 << 20  # twice the 256 MB Infinity Cache
 METRIC = "tokens/s + % bf16 MFMA peak, fused LCE fwd N=8192 D=4096 V=151936"
 # The page's own number for this workload ("Een gefuseerde forward-kernel voor
 # lineaire cross-entropy op Apple-GPU's", abstract and section 3): its fused
@@ -442,6 +444,8 @@ def main():
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="only measure the matrix-core ceiling (random and constant operands)")
     ap.add_argument("--ceiling-seconds", type=float, default=1.0)
+    ap.add_argument("--cold", action="store_true",
+                    help="forward: scrub the caches (a 512 MiB read) before each timed launch")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the headline forward (no also_measured block)")
     ap.add_argument("--also-steps", type=int, default=10, help="timed steps of each also_measured configuration")
@@ -481,14 +485,16 @@ def main():
 
 # The other configurations timed in the default run, after the headline
 # forward (each with its own warm-up and settle phase, fewer steps, no CPU
-# baseline): (label, workload, backward?, quantised-head bits)
+# baseline): (label, workload, backward?, quantised-head bits, cold caches?)
 ALSO = (
-    ("backward_prod_bf16", "prod_bf16", True, 0),
-    ("forward_quant4_prod_bf16", "prod_bf16", False, 4),
-    ("forward_small_bf16", "small_bf16", False, 0),
-    ("forward_medium_bf16", "medium_bf16", False, 0),
-    ("backward_small_bf16", "small_bf16", True, 0),
-    ("backward_medium_bf16", "medium_bf16", True, 0),
+    ("backward_prod_bf16", "prod_bf16", True, 0, False),
+    ("forward_quant4_prod_bf16", "prod_bf16", False, 4, False),
+    ("forward_small_bf16", "small_bf16", False, 0, False),
+    ("forward_medium_bf16", "medium_bf16", False, 0, False),
+    ("backward_small_bf16", "small_bf16", True, 0, False),
+    ("backward_medium_bf16", "medium_bf16", True, 0, False),
+    ("forward_prod_bf16_cold", "prod_bf16", False, 0, True),
+    ("forward_small_bf16_cold", "small_bf16", False, 0, True),
 )
 
 
@@ -498,10 +504,11 @@ def also_measured(args):
     and its fraction of the bf16 dense peak."""
     import workloads
     out = {}
-    for label, wname, backward, bits in ALSO:
+    for label, wname, backward, bits, cold in ALSO:
         sub = argparse.Namespace(**vars(args))
         sub.steps, sub.warmup, sub.settle_seconds = args.also_steps, 2, min(args.settle_seconds, 2.0)
         sub.no_cpu_baseline, sub.no_ceiling, sub.backward, sub.quant = True, True, backward, bits
+        sub.cold = cold
         w = workloads.WORKLOADS[wname]
         print(f"[bench] also: {label}", file=sys.stderr, flush=True)
         if bits:
@@ -518,6 +525,9 @@ def also_measured(args):
         if "tile_vocab" in r["config"]:
             out[label]["tile"] = f'{r["config"]["tile_vocab"]}x{r["config"]["tile_tokens"]}'
             out[label]["chunks"] = r["config"]["chunks"]
+        if cold:
+            out[label]["cold_caches"] = True
+            del out[label]["tokens_per_s"]  # the wall clock includes the cache scrubs
     return out
 
 
@@ -550,10 +560,20 @@ def bench_forward(args, w):
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    # --cold: before each timed launch, read a 512 MiB buffer on the same
+    # stream (a reduction over it), which evicts H and W from the L2s and the
+    # 256 MB Infinity Cache without leaving dirty lines behind, so the launch
+    # reads its inputs from HBM (the events time the launch only; the
+    # wall-clock rate then includes the scrubs)
+    cold = getattr(args, "cold", False)
+    scrub = torch.ones(COLD_SCRUB_BYTES // 4, dtype=torch.float32, device=dev) if cold else None
+    scrub_sink = []
+    print(f"[bench] timing {args.steps} steps{' (cold caches)' if cold else ''}", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for a, b in ev:
+        if cold:
+            scrub_sink.append(scrub.sum())
         a.record(stream)
         flce.flce_partials(H, W, y, ws, stream=stream)
         b.record(stream)
@@ -589,7 +609,7 @@ def bench_forward(args, w):
         "config": {"workload": w.name, "N": w.N, "D": w.D, "V": w.V, "input_dtype": w.dtype,
                    "tile_vocab": plan["tile_vocab"], "tile_tokens": plan["tile_tokens"],
                    "chunks": plan["chunks"], "grid": plan["grid"],
-                   "workspace_bytes": plan["workspace_bytes"]},
+                   "workspace_bytes": plan["workspace_bytes"], "cold_caches": cold},
         "mfma_fraction_of_step": flops / (ms_per_step * 1e-3) / 1e12 / peak,
         "roofline": {
             "bound": "mfma",

@@ -30,6 +30,6 @@ def test_kernel_source_hash_ignores_comments(tmp_path):
 def test_also_measured_configurations_exist():
     import bench
     import workloads
-    for label, wname, backward, bits in bench.ALSO:
+    for label, wname, backward, bits, cold in bench.ALSO:
         assert wname in workloads.WORKLOADS, label
         assert bits in (0, 4, 8)
