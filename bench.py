@@ -53,19 +53,25 @@ PAGE_TOKENS_PER_S = 8192 / 2.105
 PAGE_REF = ("the page's fused MLX/Metal forward on one Apple M1 Max: 8192 tokens in 2.105 s "
             "(3892 tokens/s); another machine, context only")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_flce_partials_prod_bf16.json")
-KERNEL_SRC = os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "flce.hip")
+# the kernels and the planners that choose their tiles and grids
+KERNEL_SRC = (os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "flce.hip"),
+              os.path.join(ROOT, "linear_cross_entropy_amd", "csrc", "flce_plan.h"))
 
 
-def kernel_source_sha(path: str = KERNEL_SRC) -> str:
-    """Hash of the kernel source with comments and whitespace removed, so that
+def kernel_source_sha(paths=KERNEL_SRC) -> str:
+    """Hash of the kernel sources with comments and whitespace removed, so that
     counters stay attached to the code they were taken on across comment edits."""
     import re
-    with open(path) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+    if isinstance(paths, str):
+        paths = (paths,)
+    texts = []
+    for path in paths:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        texts.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(texts).encode()).hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str):

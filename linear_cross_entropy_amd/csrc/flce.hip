@@ -1194,8 +1194,9 @@ int launch_backward(const BwdPlan& bp, const void* H, const void* W, const int32
 // bf16 buffer in the workspace and run through the partials kernel with its
 // chunks' partial states written after the previous slices' (and targets
 // offset by the slice's first row), then one merge covers every chunk. Vs is
-// a multiple of 3072 rows (8 chunks of 384-row tiles) with the buffer near
-// kQuantSliceBytes; a vocabulary that fits one slice is a single pass.
+// a multiple of 3072 rows (8 chunks of whole 384-row tiles; 30720 rows at
+// D = 4096 also split evenly into 320- and 256-row tiles) with the buffer
+// near kQuantSliceBytes; a vocabulary that fits one slice is a single pass.
 void launch_dequant(int bits, int D, int group, const uint8_t* codes, const float* scales, const float* biases,
                     int64_t rows, __bf16* out, hipStream_t stream) {
   const int64_t n = rows * (D / 8);

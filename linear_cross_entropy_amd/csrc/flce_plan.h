@@ -44,8 +44,9 @@ struct TileCfg {
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
   // Whether the younger wave of each SIMD takes issue priority around the
   // stage barrier (see the main loop). Measured on the production shape: the
-  // 256-row tile is 3% faster with it, the 320- and 384-row tiles up to 1%
-  // faster without it.
+  // 256-row 32x32 tile is 3% faster with it, the 320- and 384-row 32x32 tiles
+  // up to 1% faster without it, and the 320-row 16x16 tile 1.3% faster
+  // without it.
   static constexpr bool YOUNG_PRIO = BV == 256;
   static_assert(M == 32 || M == 16, "MFMA shape");
   static_assert(WV % M == 0 && WT % M == 0, "waves own whole MFMA tiles");
