@@ -1,4 +1,5 @@
-"""Seeded random shapes: forward and backward against the oracle on every row.
+"""Seeded random shapes: forward, backward and the quantised head against the
+oracle on every row.
 
 The fixed grids in parity.py are chosen by hand for known edges; these shapes
 are drawn once from a fixed seed over wide ranges (N from 1 to 6000,
@@ -75,3 +76,53 @@ def test_random_shape_backward(N, D, V, dt):
     H, W, y = _inputs(N, D, V, dt, seed=5 * N + D + 11 * V)
     g = torch.linspace(0.25, 1.75, N, dtype=torch.float32).to(DEV)
     parity_backward(H, W, y, g, what=f"random bwd N={N} D={D} V={V} {dt}")
+
+
+def _quant_shapes(seed, count, budget):
+    """count (N, D, V, bits, group): 4 or 8 bits, groups of 8 to 256. Every
+    other one has D a multiple of the group up to 4096 and N, V log-uniform;
+    the others D from 2048 to 8192 and V from 20000 to 60000 with few rows, so
+    that the head runs in several dequantisation slices (about 256 MB of bf16
+    each). N*D*V <= budget."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        bits = int(rng.choice([4, 8]))
+        group = int(rng.choice([8, 16, 32, 64, 128, 256]))
+        if len(out) % 2 == 0:
+            D = group * int(rng.integers(1, max(2, 4096 // group)))
+            N = int(np.exp(rng.uniform(0, np.log(3000))))
+            V = int(np.exp(rng.uniform(0, np.log(60000))))
+        else:
+            D = group * int(rng.integers(max(1, 2048 // group), 8192 // group + 1))
+            V = int(rng.integers(20000, 60001))
+            N = int(min(64, max(1, budget // (D * V))))
+        if N * D * V <= budget:
+            out.append((N, D, V, bits, group))
+    return out
+
+
+QUANT_SHAPES = _quant_shapes(606, 10, 3e9)
+
+
+@pytest.mark.parametrize("N,D,V,bits,group", QUANT_SHAPES, ids=lambda v: str(v))
+def test_random_shape_quant_head(N, D, V, bits, group):
+    """The quantised head's forward and frozen-head backward against the
+    oracle on the dequantised head (oracle.dequantize), every row."""
+    import oracle
+    import linear_cross_entropy_amd as flce
+    from parity import check_bwd, check_close
+    print(f"[random quant] N={N} D={D} V={V} bits={bits} group={group}", flush=True)
+    H, codes, scales, biases, y = workloads.make_quant(N, D, V, bits, group, seed=N + V + D, device=DEV,
+                                                       w_std=1.0 / np.sqrt(D))
+    loss, lse = flce.flce_forward_quant(H, codes, scales, biases, y, bits, group)
+    g = torch.linspace(0.5, 1.5, N, dtype=torch.float32, device=DEV)
+    dH = flce.flce_backward_quant(H, codes, scales, biases, y, lse, g, bits, group)
+    torch.cuda.synchronize()
+    bits16 = oracle.dequantize(codes.cpu(), scales.cpu(), biases.cpu(), bits, group)
+    Wq = torch.from_numpy(np.ascontiguousarray(bits16).view(np.int16)).view(torch.bfloat16)
+    rl, rs, _ = oracle.forward(H.cpu(), Wq, y.cpu())
+    check_close(lse.cpu().numpy(), rs, torch.bfloat16, "random quant lse")
+    check_close(loss.cpu().numpy(), rl, torch.bfloat16, "random quant loss")
+    ref = oracle.backward(H.cpu(), Wq, y.cpu(), g.cpu(), want_dW=False)
+    check_bwd(dH.cpu().numpy(), ref["dH"], ref["dH_abs"], torch.bfloat16, V, "random quant dH")
