@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from parity import BWD_SHAPES, bwd_bound, check_bwd, gpu_backward, parity_backward
+from parity import BWD_SHAPES, bwd_bound, check_bwd, check_close, gpu_backward, parity_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -230,3 +230,39 @@ def test_backward_medium_workload_sparse_gradient():
     assert np.all(dH[np.setdiff1d(np.arange(w.N), rows)] == 0.0)
     ew, rw = check_bwd(dW, ref["dW"], ref["dW_abs"], H.dtype, w.N, "medium dW")
     _log(f"[bwd] medium dH max |d| {eh:.3e} rel {rh:.2e}; dW max |d| {ew:.3e} rel {rw:.2e}")
+
+
+def test_buffers_beyond_two_gib():
+    """H of 2 GiB (N = 131072, D = 8192 bf16) and a 4 GiB dH: the last rows of H
+    start beyond 2^31 bytes and those of dH beyond 2^32, so every row offset
+    must be computed in 64 bits (the buffer resources are made per row block).
+    Forward on sampled rows including the last ones; backward with the
+    gradient on 10 rows spread over the batch: those dH rows and all of dW
+    against the oracle, every other dH row exactly 0 (checked on the GPU)."""
+    import linear_cross_entropy_amd as flce
+    N, D, V = 131072, 8192, 4000
+    _log(f"[big buffers] N={N} D={D} V={V} bf16")
+    H, W, y = workloads.make_custom(N, D, V, "bf16", seed=2031, device=DEV, h_std=1.0, w_std=1.0 / D ** 0.5)
+    assert H.numel() * H.element_size() >= 2 ** 31
+    rows = np.array([0, 1, 255, 256, 65535, 65536, 131000, 131069, 131070, 131071])
+    y[torch.as_tensor(rows[-4:], device=DEV)] = torch.tensor([0, V - 1, 1234, V - 2], dtype=torch.int32, device=DEV)
+    loss, lse = flce.flce_forward(H, W, y)
+    torch.cuda.synchronize()
+    Hc, Wc, yc = H.cpu(), W.cpu(), y.cpu()
+    rl, rs, _ = oracle.forward(Hc, Wc, yc, rows=rows)
+    check_close(lse.cpu().numpy()[rows], rs, H.dtype, "big buffers lse")
+    check_close(loss.cpu().numpy()[rows], rl, H.dtype, "big buffers loss")
+    g = torch.zeros(N, dtype=torch.float32)
+    g[torch.as_tensor(rows)] = torch.linspace(0.5, 1.5, len(rows))
+    g = g.to(DEV)
+    dH, dW = flce.flce_backward(H, W, y, lse, g)
+    torch.cuda.synchronize()
+    assert dH.numel() * dH.element_size() >= 2 ** 32
+    mask = torch.ones(N, dtype=torch.bool, device=DEV)
+    mask[torch.as_tensor(rows, device=DEV)] = False
+    assert bool((dH[mask] == 0).all().item()), "dH nonzero off the gradient rows"
+    sel = torch.as_tensor(rows, dtype=torch.long)
+    ref = oracle.backward(Hc[sel], Wc, yc[sel], g.cpu()[sel])
+    check_bwd(dH[sel.to(DEV)].cpu().numpy(), ref["dH"], ref["dH_abs"], H.dtype, V, "big buffers dH rows")
+    e, rel = check_bwd(dW.cpu().numpy(), ref["dW"], ref["dW_abs"], H.dtype, N, "big buffers dW")
+    _log(f"[big buffers] dW max |d| {e:.3e}, relative Frobenius error {rel:.2e}")
